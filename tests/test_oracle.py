@@ -1,0 +1,542 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+Each test names the passage it follows.  None of them re-types the oracle's
+own loops: they use printed worked examples, closed forms, library routines
+(numpy's float16 decoding, scipy's softmax / logsumexp), 40-digit decimal brute
+force on tiny inputs, and invariances the pages claim.
+"""
+from decimal import Decimal, getcontext
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synth
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def contiguous_problem(q, k, v, scale=None, seq_lens=None):
+    """q [B,Hq,d], k/v [B,N,Hkv,d] float32 -> (problem, args)."""
+    B, Hq, d = q.shape
+    _, N, Hkv, _ = k.shape
+    p = oracle.problem(B, Hq, Hkv, d, "f32", N=N, scale=scale)
+    return p, (q.astype(np.float32), k.astype(np.float32), v.astype(np.float32))
+
+
+def scalar_row_problem(scores, vvals, d=64):
+    """One request, one head, whose scaled scores are exactly `scores` and whose
+    first V coordinate is `vvals` (all other coordinates 0).  q = 8 e0 with d = 64
+    makes q.k / sqrt(64) = k0 exactly."""
+    n = len(scores)
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = math.sqrt(d)
+    k = np.zeros((1, n, 1, d), np.float32)
+    v = np.zeros((1, n, 1, d), np.float32)
+    k[0, :, 0, 0] = scores
+    v[0, :, 0, 0] = vvals
+    return contiguous_problem(q, k, v)
+
+
+getcontext().prec = 40
+
+
+def brute_force(q, k, v, scale, lens=None, table=None, page=0):
+    """40-digit decimal softmax attention straight from the definition."""
+    B, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    sc = Decimal(1) / Decimal(d).sqrt() if scale is None else Decimal(float(scale))
+    outs = np.zeros((B * Hq, d))
+    lses = np.zeros(B * Hq)
+    for b in range(B):
+        n = k.shape[1] if lens is None else int(lens[b])
+        for h in range(Hq):
+            kvh = h // G
+            rows = []
+            for t in range(n):
+                if page:
+                    phys = table[b, t // page]
+                    rows.append((k[phys, t % page, kvh], v[phys, t % page, kvh]))
+                else:
+                    rows.append((k[b, t, kvh], v[b, t, kvh]))
+            s = [sum(Decimal(float(a)) * Decimal(float(c)) for a, c in zip(q[b, h], kr)) * sc for kr, _ in rows]
+            m = max(s)
+            w = [(x - m).exp() for x in s]
+            Z = sum(w)
+            for i in range(d):
+                outs[b * Hq + h, i] = float(sum(wi * Decimal(float(vr[i])) for wi, (_, vr) in zip(w, rows)) / Z)
+            lses[b * Hq + h] = float(m + Z.ln())
+    return outs, lses
+
+
+# ----------------------------------------------------------------------------
+# storage decoding
+# ----------------------------------------------------------------------------
+def test_decode_f16_all_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    got = oracle.decode(h, "f16")
+    np.testing.assert_array_equal(got, h.astype(np.float64))
+
+
+def test_decode_bf16_all_patterns_match_fp32_widening():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = oracle.decode(bits, "bf16")
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------
+# the handbook's worked online-softmax exercise
+# ----------------------------------------------------------------------------
+def test_worked_exercise_attention(golden):
+    g = golden("handbook_online_softmax_exercise.json")
+    p, (q, k, v) = scalar_row_problem(g["scores"], g["v"])
+    out, lse = oracle.attention(p, q, k, v)
+    assert abs(out[0, 0] - g["final"]) <= g["tol"]["final"]
+    assert np.all(out[0, 1:] == 0.0)
+    w = np.exp(np.array(g["scores"]))
+    np.testing.assert_allclose(w, g["direct_weights"], atol=g["tol"]["direct_weights"])
+    assert abs(w.sum() - g["direct_weight_sum"]) <= g["tol"]["direct_weight_sum"]
+    assert abs(lse[0] - math.log(g["direct_weight_sum"])) < 1e-3
+
+
+def test_worked_exercise_tile_trace(golden):
+    g = golden("handbook_online_softmax_exercise.json")
+    v = np.array(g["v"])[:, None]
+    out, lse, tm, tl, ta = oracle.online_tiles(np.array(g["scores"]), v, g["tile"])
+    tol = g["tol"]
+    assert tm[0] == g["tile1"]["m"] and tm[1] == g["tile2"]["m"]
+    assert abs(tl[0] - g["tile1"]["l"]) <= tol["l"]
+    assert abs(tl[1] - g["tile2"]["l"]) <= tol["l"]
+    assert abs(ta[0, 0] - g["tile1"]["acc"]) <= tol["acc"]
+    assert abs(ta[1, 0] - g["tile2"]["acc"]) <= tol["acc"]
+    assert abs(math.exp(g["tile1"]["m"] - g["tile2"]["m"]) - g["tile2"]["correction"]) <= tol["p"]
+    assert abs(out[0] - g["final"]) <= tol["final"]
+
+
+def test_worked_exercise_split_partials_and_merge(golden):
+    """Split size 2 reproduces the two tiles as two splits (normalised O_s)."""
+    g = golden("handbook_online_softmax_exercise.json")
+    p, (q, k, v) = scalar_row_problem(g["scores"], g["v"])
+    po, pm, pl = oracle.split_partials(p, q, k, v, split=2, S_max=2)
+    assert pm[0, 0] == 3.0 and pm[0, 1] == 5.0
+    assert abs(pl[0, 0] - g["tile1"]["l"]) <= g["tol"]["l"]
+    # the page's first-tile accumulator is unnormalised: O_1 * l_1
+    assert abs(po[0, 0, 0] * pl[0, 0] - g["tile1"]["acc"]) <= g["tol"]["acc"]
+    assert abs(pl[0, 1] - sum(g["tile2"]["p"])) <= g["tol"]["p"] * 2
+    for form in ("max", "lse"):
+        out, lse = oracle.merge(po, pm, pl, form=form)
+        assert abs(out[0, 0] - g["final"]) <= g["tol"]["final"]
+    # merged denominator relative to the global max: the page's 1.2034
+    lglob = pl[0, 0] * math.exp(pm[0, 0] - 5.0) + pl[0, 1]
+    assert abs(lglob - g["tile2"]["l"]) <= g["tol"]["l"]
+
+
+def test_worked_exercise_decimal_value():
+    p, (q, k, v) = scalar_row_problem([1, 3, 2, 5], [10, 20, 30, 40])
+    out, lse = oracle.attention(p, q, k, v)
+    bo, bl = brute_force(q, k, v, None)
+    assert abs(out[0, 0] - bo[0, 0]) < 1e-12 and abs(lse[0] - bl[0]) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny inputs
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_contiguous(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, Hq, Hkv, d, N = 2, 4, 2, 4, 6
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32) * 2
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 2
+    v = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    lens = np.array([6, 3], np.int32)
+    p, args = contiguous_problem(q, k, v)
+    out, lse = oracle.attention(p, *args, seq_lens=lens)
+    bo, bl = brute_force(q, k, v, None, lens=lens)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_brute_force_paged():
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, d, page = 3, 4, 2, 4, 2
+    lens = np.array([5, 1, 4], np.int32)
+    nblk = (lens + page - 1) // page
+    P = int(nblk.sum())
+    perm = rng.permutation(P)
+    table = np.full((B, 3), -1, np.int32)
+    nx = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[nx:nx + nblk[b]]
+        nx += nblk[b]
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((P, page, Hkv, d)).astype(np.float32)
+    v = rng.standard_normal((P, page, Hkv, d)).astype(np.float32)
+    p = oracle.problem(B, Hq, Hkv, d, "f32", page_size=page, max_blocks=3)
+    out, lse = oracle.attention(p, q, k, v, seq_lens=lens, block_table=table)
+    bo, bl = brute_force(q, k, v, None, lens=lens, table=table, page=page)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_brute_force_f16_and_bf16_storage():
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, d, N = 1, 2, 1, 8, 5
+    for dt in ("f16", "bf16"):
+        qf = rng.standard_normal((B, Hq, d)).astype(np.float32)
+        kf = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+        vf = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+        q, k, v = (synth.encode(x, dt) for x in (qf, kf, vf))
+        p = oracle.problem(B, Hq, Hkv, d, dt, N=N)
+        out, lse = oracle.attention(p, q, k, v)
+        # the brute force reads the exactly decoded values
+        dq, dk, dv = (synth.decode_f64(x, dt) for x in (q, k, v))
+        bo, bl = brute_force(dq, dk, dv, None)
+        np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_explicit_scale_argument():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 4)).astype(np.float32)
+    k = rng.standard_normal((1, 4, 1, 4)).astype(np.float32)
+    v = rng.standard_normal((1, 4, 1, 4)).astype(np.float32)
+    p, args = contiguous_problem(q, k, v, scale=0.3)
+    out, lse = oracle.attention(p, *args)
+    bo, bl = brute_force(q, k, v, 0.3)
+    np.testing.assert_allclose(out, bo, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# a special case that reduces to library routines
+# ----------------------------------------------------------------------------
+def test_identity_v_gives_scipy_softmax_and_logsumexp():
+    """With V = I (d = N), the output row is the attention weight vector."""
+    rng = np.random.default_rng(11)
+    N = d = 16
+    q = rng.standard_normal((1, 1, d)).astype(np.float32) * 3
+    k = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    v = np.eye(N, dtype=np.float32).reshape(1, N, 1, d)
+    p, args = contiguous_problem(q, k, v)
+    out, lse = oracle.attention(p, *args)
+    s = (k[0, :, 0, :].astype(np.float64) @ q[0, 0].astype(np.float64)) / math.sqrt(d)
+    np.testing.assert_allclose(out[0], scipy.special.softmax(s), rtol=1e-13, atol=1e-15)
+    assert abs(lse[0] - scipy.special.logsumexp(s)) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+def test_single_token_returns_its_value_row_bitwise():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((2, 4, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 1, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 1, 2, 8)).astype(np.float32)
+    p, args = contiguous_problem(q, k, v)
+    out, lse = oracle.attention(p, *args)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out[b * 4 + h], v[b, 0, h // 2].astype(np.float64))
+            s = float(np.dot(q[b, h].astype(np.float64), k[b, 0, h // 2].astype(np.float64))) / math.sqrt(8)
+            assert abs(lse[b * 4 + h] - s) < 1e-14
+
+
+def test_identical_value_rows_return_that_row():
+    rng = np.random.default_rng(2)
+    N, d = 300, 16
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    k = rng.standard_normal((1, N, 1, d)).astype(np.float32) * 3
+    row = rng.standard_normal(d).astype(np.float32)
+    v = np.broadcast_to(row, (1, N, 1, d)).copy()
+    p, args = contiguous_problem(q, k, v)
+    out, _ = oracle.attention(p, *args)
+    np.testing.assert_allclose(out, np.broadcast_to(row.astype(np.float64), (2, d)), rtol=1e-14, atol=1e-15)
+
+
+def test_equal_scores_give_mean_of_v_and_log_n():
+    rng = np.random.default_rng(3)
+    N, d = 257, 8
+    q = np.zeros((1, 1, d), np.float32)
+    k = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    v = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    p, args = contiguous_problem(q, k, v)
+    out, lse = oracle.attention(p, *args)
+    np.testing.assert_allclose(out[0], v[0, :, 0, :].astype(np.float64).mean(axis=0), rtol=1e-13, atol=1e-15)
+    assert lse[0] == math.log(N)
+
+
+def test_shift_of_all_scores_leaves_output_and_shifts_lse():
+    """k_t += (c sqrt(d) / |q|^2) q adds c to every scaled score."""
+    rng = np.random.default_rng(4)
+    N, d, c = 64, 16, 3.0
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, N, 1, d))
+    v = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    alpha = c * math.sqrt(d) / float(q[0, 0] @ q[0, 0])
+    # f32 storage rounds the shifted keys, so compare to the rounding level
+    p, a0 = contiguous_problem(q.astype(np.float32), k.astype(np.float32), v)
+    p1, a1 = contiguous_problem(q.astype(np.float32), (k + alpha * q[0, 0]).astype(np.float32), v)
+    o0, l0 = oracle.attention(p, *a0)
+    o1, l1 = oracle.attention(p1, *a1)
+    np.testing.assert_allclose(o1, o0, atol=2e-5)
+    assert abs(l1[0] - (l0[0] + c)) < 1e-4
+
+
+def test_gqa_head_mapping_consecutive_heads_share_kv_head():
+    """V of KV head j is the constant j + 1, so query head h must return h // G + 1."""
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, d, N = 2, 8, 2, 4, 10
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    v = np.zeros((B, N, Hkv, d), np.float32)
+    for j in range(Hkv):
+        v[:, :, j, :] = j + 1
+    p, args = contiguous_problem(q, k, v)
+    out, _ = oracle.attention(p, *args)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[b * Hq + h], h // G + 1, rtol=1e-14)
+
+
+def test_empty_request_gives_zero_and_minus_inf():
+    q = np.ones((2, 1, 4), np.float32)
+    k = np.ones((2, 3, 1, 4), np.float32)
+    v = np.ones((2, 3, 1, 4), np.float32)
+    p, args = contiguous_problem(q, k, v)
+    out, lse = oracle.attention(p, *args, seq_lens=np.array([0, 3], np.int32))
+    assert np.all(out[0] == 0) and lse[0] == -np.inf
+    np.testing.assert_allclose(out[1], 1.0)
+
+
+# ----------------------------------------------------------------------------
+# paged indexing
+# ----------------------------------------------------------------------------
+def _paged_inputs(seed=0, page=16, lens=(1, 15, 16, 17, 255, 256, 257, 1000)):
+    w = synth.with_lens(synth.Workload("t", B=1, Hq=4, Hkv=2, d=16, dtype="f32", split=32, N=16,
+                                       page_size=page), lens)
+    return synth.make_inputs(w, poison_tail=True)
+
+
+def test_paged_equals_logically_contiguous_copy_bitwise():
+    inp = _paged_inputs()
+    w = inp.w
+    p = oracle.problem_of(inp)
+    out_p, lse_p = oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table)
+    # gather into a contiguous [B, N, Hkv, d] cache in logical order
+    kc = np.zeros((w.B, w.N, w.Hkv, w.d), np.float32)
+    vc = np.zeros_like(kc)
+    for b in range(w.B):
+        for t in range(int(inp.seq_lens[b])):
+            phys = inp.block_table[b, t // w.page_size]
+            kc[b, t] = inp.k[phys, t % w.page_size]
+            vc[b, t] = inp.v[phys, t % w.page_size]
+    pc = oracle.problem(w.B, w.Hq, w.Hkv, w.d, "f32", N=w.N)
+    out_c, lse_c = oracle.attention(pc, inp.q, kc, vc, seq_lens=inp.seq_lens)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    assert np.isfinite(out_p).all()     # the NaN-poisoned tail slots were never read
+
+
+def test_paged_probe_reads_the_page_formula_location():
+    """V rows encode their physical (block, slot); one key per request is boosted so
+    the softmax is one-hot on a chosen logical token t*.  The output names the
+    physical row that the page's formula (slot t % page of block table[t / page])
+    assigns to t*."""
+    inp = _paged_inputs()
+    w = inp.w
+    P = inp.k.shape[0]
+    k = np.zeros_like(inp.k)
+    v = np.zeros_like(inp.v)
+    for phys in range(P):
+        for slot in range(w.page_size):
+            v[phys, slot, :, 0] = phys
+            v[phys, slot, :, 1] = slot
+    q = np.zeros_like(inp.q)
+    q[:, :, 0] = 1.0
+    targets = []
+    for b in range(w.B):
+        n = int(inp.seq_lens[b])
+        t_star = (7 * b + 3) % n
+        phys = inp.block_table[b, t_star // w.page_size]
+        k[phys, t_star % w.page_size, :, 0] = 400.0     # score 100 vs 0 elsewhere
+        targets.append((phys, t_star % w.page_size))
+    p = oracle.problem_of(inp)
+    out, _ = oracle.attention(p, q, k, v, seq_lens=inp.seq_lens, block_table=inp.block_table)
+    # every other weight is e^-100 relative, far below half an ulp of the result
+    for b, (phys, slot) in enumerate(targets):
+        for h in range(w.Hq):
+            r = b * w.Hq + h
+            assert out[r, 0] == phys and out[r, 1] == slot, (b, h, out[r, :2], phys, slot)
+
+
+# ----------------------------------------------------------------------------
+# split-KV: invariance to the split count and to the merge order
+# ----------------------------------------------------------------------------
+def _random_problem(seed=9, B=2, Hq=4, Hkv=2, d=8, N=100, lens=(100, 37)):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32) * 2
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    v = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    p, args = contiguous_problem(q, k, v)
+    return p, args, np.array(lens, np.int32)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 16, 64, 100])
+def test_split_count_invariance(split):
+    p, args, lens = _random_problem()
+    ref, lref = oracle.attention(p, *args, seq_lens=lens)
+    S = -(-100 // split)
+    po, pm, pl = oracle.split_partials(p, *args, split=split, S_max=S, seq_lens=lens)
+    for form in ("max", "lse"):
+        out, lse = oracle.merge(po, pm, pl, form=form)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lref, rtol=0, atol=1e-12)
+
+
+def test_merge_order_invariance():
+    p, args, lens = _random_problem()
+    po, pm, pl = oracle.split_partials(p, *args, split=8, S_max=13, seq_lens=lens)
+    o0, l0 = oracle.merge(po, pm, pl)
+    perm = np.random.default_rng(1).permutation(13)
+    o1, l1 = oracle.merge(po[:, perm], pm[:, perm], pl[:, perm])
+    np.testing.assert_allclose(o1, o0, atol=1e-13)
+    np.testing.assert_allclose(l1, l0, atol=1e-13)
+
+
+def test_partials_of_a_short_request_mark_empty_splits():
+    p, args, lens = _random_problem()
+    po, pm, pl = oracle.split_partials(p, *args, split=16, S_max=7, seq_lens=lens)
+    # request 1 has 37 tokens -> splits 0..2 hold 16, 16, 5 tokens; 3..6 are empty
+    Hq = p.Hq
+    for h in range(Hq):
+        r = Hq + h
+        assert np.all(pl[r, :3] > 0) and np.all(pl[r, 3:] == 0)
+        assert np.all(pm[r, 3:] == -np.inf)
+
+
+def test_merge_skips_empty_splits_and_never_returns_nan():
+    rng = np.random.default_rng(2)
+    S, d = 5, 4
+    po = rng.standard_normal((3, S, d))
+    pm = rng.standard_normal((3, S))
+    pl = rng.random((3, S)) + 0.5
+    # row 0: two empty splits; row 1: all empty; row 2: untouched
+    pm[0, [1, 3]] = -np.inf
+    pl[0, [1, 3]] = 0.0
+    po[0, [1, 3]] = np.nan         # an empty split's O must not be read
+    pm[1] = -np.inf
+    pl[1] = 0.0
+    for form in ("max", "lse"):
+        out, lse = oracle.merge(po, pm, pl, form=form)
+        assert np.isfinite(out).all()
+        ref0, lref0 = oracle.merge(po[:1, [0, 2, 4]], pm[:1, [0, 2, 4]], pl[:1, [0, 2, 4]], form=form)
+        np.testing.assert_allclose(out[0], ref0[0], atol=1e-14)
+        assert np.all(out[1] == 0) and lse[1] == -np.inf
+
+
+def test_merge_forms_agree_with_a_direct_closed_form():
+    """Two splits with known (m, l, O): the merge is the l e^m weighted mean."""
+    po = np.array([[[1.0, 2.0], [3.0, -1.0]]])
+    pm = np.array([[0.5, 2.0]])
+    pl = np.array([[2.0, 0.25]])
+    w = pl[0] * np.exp(pm[0])
+    want = (w[:, None] * po[0]).sum(0) / w.sum()
+    for form in ("max", "lse"):
+        out, lse = oracle.merge(po, pm, pl, form=form)
+        np.testing.assert_allclose(out[0], want, rtol=1e-15)
+        assert abs(lse[0] - math.log(w.sum())) < 1e-14
+
+
+# ----------------------------------------------------------------------------
+# unified max value
+# ----------------------------------------------------------------------------
+def test_figure6_range_predicate(golden):
+    g = golden("fdpp_figure6_range_check.json")
+    lo, hi = g["phi"] + g["a"], g["phi"] + g["b"]
+    for case in g["cases"]:
+        sc = case["scores"]
+        for s_idx, flag in enumerate(case["flagged_splits"]):
+            part = sc[s_idx * g["split"]:(s_idx + 1) * g["split"]]
+            assert any(oracle.out_of_range(x, lo, hi) for x in part) == bool(flag)
+
+
+def test_figure6_through_unified_max(golden):
+    g = golden("fdpp_figure6_range_check.json")
+    lo, hi = g["phi"] + g["a"], g["phi"] + g["b"]
+    for case in g["cases"]:
+        p, (q, k, v) = scalar_row_problem(case["scores"], [1.0, 2.0, 3.0, 4.0])
+        r = oracle.unified_max(p, q, k, v, split=2, S_max=2, phi=g["phi"], lo=lo, hi=hi)
+        assert list(r["flags"][0]) == case["flagged_splits"]
+        exact, else_ = oracle.attention(p, q, k, v)
+        np.testing.assert_allclose(r["out"], exact, atol=1e-13)
+        # unflagged splits keep phi; a flagged split uses its own max
+        for s_idx, flag in enumerate(case["flagged_splits"]):
+            part = case["scores"][2 * s_idx:2 * s_idx + 2]
+            assert r["part_m"][0, s_idx] == (max(part) if flag else g["phi"])
+
+
+@pytest.mark.parametrize("offset", [-40.0, -10.0, 0.0, 7.5, 40.0])
+def test_unified_max_is_independent_of_phi(offset):
+    p, args, lens = _random_problem(seed=12)
+    exact, lexact = oracle.attention(p, *args, seq_lens=lens)
+    phi = offset                   # scores are O(1): phi from far below to far above the max
+    r = oracle.unified_max(p, *args, split=16, S_max=7, phi=phi, lo=-np.inf, hi=np.inf, seq_lens=lens)
+    assert r["n_flagged"] == 0
+    np.testing.assert_allclose(r["out"], exact, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lexact, rtol=0, atol=1e-11)
+
+
+def test_unified_max_all_flagged_equals_synchronized_partials_bitwise():
+    p, args, lens = _random_problem(seed=13)
+    sp_o, sp_m, sp_l = oracle.split_partials(p, *args, split=16, S_max=7, seq_lens=lens)
+    r = oracle.unified_max(p, *args, split=16, S_max=7, phi=0.0, lo=1e30, hi=1e31, seq_lens=lens)
+    valid = sp_l > 0
+    assert r["n_flagged"] == int(valid.sum())
+    np.testing.assert_array_equal(r["flags"].astype(bool), valid)
+    np.testing.assert_array_equal(r["part_m"], sp_m)
+    np.testing.assert_array_equal(r["part_l"], sp_l)
+    np.testing.assert_array_equal(r["part_o"], sp_o)
+
+
+def test_unified_max_flag_rate_matches_closed_form():
+    """Stress recipe: key rows scaled x8 with probability 0.02.  For a fixed q, a
+    clean score is N(0, |q|^2/d) and a stressed one N(0, 64|q|^2/d); a split of L
+    tokens is flagged with probability 1 - (1 - p_tok)^L where p_tok is the
+    two-sided tail beyond [-c, c] of that mixture."""
+    w = synth.Workload("stress_small", B=2, Hq=16, Hkv=16, d=128, dtype="bf16", split=256, N=4096,
+                       stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(w)
+    p = oracle.problem_of(inp)
+    c = 12.0
+    r = oracle.unified_max(p, inp.q, inp.k, inp.v, split=w.split, S_max=w.max_splits, phi=-c, lo=-c, hi=c)
+    qf = synth.decode_f64(inp.q, w.dtype)
+    sig = np.linalg.norm(qf, axis=-1).reshape(-1) / math.sqrt(w.d)
+    tail = lambda x: math.erfc(x / math.sqrt(2.0))      # P(|Z| > x)
+    expected = 0.0
+    var = 0.0
+    for s in sig:
+        pt = 0.98 * tail(c / s) + 0.02 * tail(c / (8 * s))
+        ps = 1 - (1 - pt) ** w.split
+        expected += ps * w.max_splits
+        var += ps * (1 - ps) * w.max_splits
+    got = r["n_flagged"]
+    assert abs(got - expected) < 5 * math.sqrt(var) + 1, (got, expected, var)
+    assert 0.2 < got / (sig.size * w.max_splits) < 0.8      # the closed form puts it near one half
+    # and the fallback keeps the result exact
+    exact, _ = oracle.attention(p, inp.q, inp.k, inp.v)
+    np.testing.assert_allclose(r["out"], exact, rtol=1e-10, atol=1e-12)
+
+
+def test_oracle_rejects_bad_shapes():
+    q = np.zeros((1, 3, 4), np.float32)
+    k = np.zeros((1, 2, 2, 4), np.float32)
+    p = oracle.problem(1, 3, 2, 4, "f32", N=2)       # Hq not a multiple of Hkv
+    with pytest.raises(ValueError):
+        oracle.attention(p, q, k, k)
