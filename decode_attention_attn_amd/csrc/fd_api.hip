@@ -1,0 +1,227 @@
+// fd_api.hip -- host side of the C ABI declared in include/fd_decode_attn.h:
+// argument validation, the split heuristic, workspace layout and kernel
+// dispatch.  Nothing here allocates, synchronises or touches device memory.
+#include <math.h>
+#include <string.h>
+
+#include "fd_decode_attn.h"
+#include "fd_internal.h"
+
+#define FD_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using fd::kMaxGroup;
+using fd::kMaxSplits;
+using fd::kMaxSplitSize;
+
+bool finite(float x) { return isfinite(x) != 0; }
+
+fd_status validate_desc(const fd_decode_desc *d) {
+    if (!d) return FD_ERR_INVALID_ARG;
+    if (d->B < 0 || d->B > 65535 || d->Hq <= 0 || d->Hkv <= 0 || d->Hkv > 65535) return FD_ERR_INVALID_ARG;
+    if (d->Hq % d->Hkv) return FD_ERR_INVALID_ARG;
+    if (d->Hq / d->Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
+    if (d->d != 64 && d->d != 128) return FD_ERR_UNSUPPORTED;
+    if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_BF16) return FD_ERR_INVALID_ARG;
+    if (d->out_dtype < FD_F32 || d->out_dtype > FD_BF16) return FD_ERR_INVALID_ARG;
+    if (d->split_size < 1 || d->split_size > kMaxSplitSize) return FD_ERR_INVALID_ARG;
+    if (d->max_splits < 1 || d->max_splits > kMaxSplits) return FD_ERR_INVALID_ARG;
+    if ((int64_t)d->max_splits * d->split_size > INT32_MAX) return FD_ERR_INVALID_ARG;
+    if (!finite(d->scale)) return FD_ERR_INVALID_ARG;
+    if (d->mode != FD_SOFTMAX_SYNC && d->mode != FD_SOFTMAX_UNIFIED_MAX) return FD_ERR_INVALID_ARG;
+    if (d->mode == FD_SOFTMAX_UNIFIED_MAX) {
+        if (!finite(d->phi) || !finite(d->lo) || !finite(d->hi)) return FD_ERR_INVALID_ARG;
+        if (!(d->lo <= d->hi)) return FD_ERR_INVALID_ARG;
+        // exp(s - phi) must stay a finite, normal fp32 number for every in-range score
+        if (fabsf(d->lo - d->phi) > fd::kMaxUnifiedRange || fabsf(d->hi - d->phi) > fd::kMaxUnifiedRange)
+            return FD_ERR_INVALID_ARG;
+    }
+    if (d->kernel < FD_KERNEL_AUTO || d->kernel > FD_KERNEL_MFMA) return FD_ERR_INVALID_ARG;
+    return FD_OK;
+}
+
+fd::PartialParams base_params(const fd_decode_desc *d) {
+    fd::PartialParams p;
+    memset(&p, 0, sizeof p);
+    p.B = d->B;
+    p.Hq = d->Hq;
+    p.Hkv = d->Hkv;
+    p.G = d->Hq / d->Hkv;
+    p.d = d->d;
+    p.split = d->split_size;
+    p.max_splits = d->max_splits;
+    const double scale = d->scale > 0.f ? (double)d->scale : (double)(1.0f / sqrtf((float)d->d));
+    const double log2e = 1.4426950408889634;
+    p.scale_log2 = (float)(scale * log2e);
+    p.unified = d->mode == FD_SOFTMAX_UNIFIED_MAX;
+    p.phi2 = (float)((double)d->phi * log2e);
+    p.lo2 = (float)((double)d->lo * log2e);
+    p.hi2 = (float)((double)d->hi * log2e);
+    p.dtype = d->kv_dtype;
+    return p;
+}
+
+fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t stream) {
+    bool mfma = false;
+    if (d->kernel == FD_KERNEL_MFMA) {
+        if (!fd::mfma_supports(p)) return FD_ERR_UNSUPPORTED;
+        mfma = true;
+    } else if (d->kernel == FD_KERNEL_AUTO) {
+        mfma = fd::mfma_supports(p);
+    }
+    const hipError_t e = mfma ? fd::launch_partial_mfma(p, stream) : fd::launch_partial_valu(p, stream);
+    return e == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WorkspaceLayout {
+    size_t o_bytes, m_bytes, total;
+};
+
+WorkspaceLayout layout(const fd_decode_desc *d) {
+    const size_t rows = (size_t)d->B * d->Hq * d->max_splits;
+    WorkspaceLayout w;
+    w.o_bytes = round256(rows * d->d * sizeof(float));
+    w.m_bytes = round256(rows * sizeof(float));
+    w.total = w.o_bytes + 2 * w.m_bytes;
+    return w;
+}
+
+fd_status run_combine(const fd_decode_desc *d, const float *part_o, const float *part_m, const float *part_l,
+                      const int32_t *seq_lens, void *out, float *lse, hipStream_t stream) {
+    fd::CombineParams c;
+    c.part_o = part_o;
+    c.part_m = part_m;
+    c.part_l = part_l;
+    c.seq_lens = seq_lens;
+    c.out = out;
+    c.lse = lse;
+    c.B = d->B;
+    c.Hq = d->Hq;
+    c.d = d->d;
+    c.split = d->split_size;
+    c.max_splits = d->max_splits;
+    c.out_dtype = d->out_dtype;
+    return fd::launch_combine(c, stream) == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+}  // namespace
+
+FD_API fd_status fd_decode_attn_partial(const fd_decode_desc *desc, const void *q, const void *k, const void *v,
+                                        int32_t kv_capacity, const int32_t *seq_lens, float *part_o,
+                                        float *part_m, float *part_l, uint8_t *flags, int32_t *fallback_count,
+                                        void *stream) {
+    fd_status st = validate_desc(desc);
+    if (st != FD_OK) return st;
+    if (kv_capacity < 0) return FD_ERR_INVALID_ARG;
+    if (desc->B == 0) return FD_OK;
+    if (!q || !k || !v || !part_o || !part_m || !part_l) return FD_ERR_INVALID_ARG;
+    fd::PartialParams p = base_params(desc);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.seq_lens = seq_lens;
+    p.kv_capacity = kv_capacity;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
+    p.flags = flags;
+    p.fallback_count = fallback_count;
+    return run_partial(desc, p, static_cast<hipStream_t>(stream));
+}
+
+FD_API fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float *part_o, const float *part_m,
+                                        const float *part_l, const int32_t *seq_lens, void *out, float *lse,
+                                        void *stream) {
+    fd_status st = validate_desc(desc);
+    if (st != FD_OK) return st;
+    if (desc->B == 0) return FD_OK;
+    if (!part_o || !part_m || !part_l || !out) return FD_ERR_INVALID_ARG;
+    return run_combine(desc, part_o, part_m, part_l, seq_lens, out, lse, static_cast<hipStream_t>(stream));
+}
+
+FD_API size_t fd_workspace_bytes(const fd_decode_desc *desc) {
+    if (validate_desc(desc) != FD_OK) return 0;
+    return layout(desc).total;
+}
+
+FD_API fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q, const void *k_cache,
+                                      const void *v_cache, int32_t num_pages, int32_t page_size,
+                                      const int32_t *block_table, int32_t max_blocks_per_seq,
+                                      const int32_t *seq_lens, void *workspace, size_t workspace_bytes, void *out,
+                                      float *lse, uint8_t *flags, int32_t *fallback_count, void *stream) {
+    fd_status st = validate_desc(desc);
+    if (st != FD_OK) return st;
+    if (page_size < 1 || num_pages < 0 || max_blocks_per_seq < 1) return FD_ERR_INVALID_ARG;
+    if (desc->split_size % page_size) return FD_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * page_size > INT32_MAX) return FD_ERR_INVALID_ARG;
+    if (desc->B == 0) return FD_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !workspace || !out) return FD_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return FD_ERR_INVALID_ARG;
+    const WorkspaceLayout w = layout(desc);
+    if (workspace_bytes < w.total) return FD_ERR_WORKSPACE_TOO_SMALL;
+    char *ws = static_cast<char *>(workspace);
+    float *part_o = reinterpret_cast<float *>(ws);
+    float *part_m = reinterpret_cast<float *>(ws + w.o_bytes);
+    float *part_l = reinterpret_cast<float *>(ws + w.o_bytes + w.m_bytes);
+
+    fd::PartialParams p = base_params(desc);
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.seq_lens = seq_lens;
+    p.block_table = block_table;
+    p.page_size = page_size;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_pages = num_pages;
+    p.kv_capacity = max_blocks_per_seq * page_size;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
+    p.flags = flags;
+    p.fallback_count = fallback_count;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_partial(desc, p, s);
+    if (st != FD_OK) return st;
+    return run_combine(desc, part_o, part_m, part_l, seq_lens, out, lse, s);
+}
+
+FD_API fd_status fd_split_heuristic(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                                    int32_t num_cus, int32_t *split_size_out, int32_t *num_splits_out) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_seq_len < 0 || page_size < 0 || num_cus < 1)
+        return FD_ERR_INVALID_ARG;
+    if (!split_size_out || !num_splits_out) return FD_ERR_INVALID_ARG;
+    const int64_t unit = page_size > 0 ? page_size : 1;
+    const int64_t n = max_seq_len > 0 ? max_seq_len : 1;
+    const int64_t work = (int64_t)B * Hkv;
+    int64_t split;
+    if (work >= 2 * (int64_t)num_cus) {
+        split = (n + unit - 1) / unit * unit;             // no split: one split covers the sequence
+    } else {
+        const int64_t want = (2 * (int64_t)num_cus + work - 1) / work;   // splits per (request, KV head)
+        split = (n + want - 1) / want;
+        if (split < 128) split = 128;
+        if (split > 256) split = 256;
+        split = (split + unit - 1) / unit * unit;         // whole pages
+    }
+    if (split > kMaxSplitSize) split = (kMaxSplitSize / unit) * unit;
+    if (split < 1) return FD_ERR_UNSUPPORTED;
+    const int64_t S = (n + split - 1) / split;
+    if (S > kMaxSplits) return FD_ERR_UNSUPPORTED;
+    *split_size_out = (int32_t)split;
+    *num_splits_out = (int32_t)S;
+    return FD_OK;
+}
+
+FD_API const char *fd_status_string(fd_status status) {
+    switch (status) {
+    case FD_OK: return "FD_OK";
+    case FD_ERR_INVALID_ARG: return "FD_ERR_INVALID_ARG";
+    case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
+    case FD_ERR_WORKSPACE_TOO_SMALL: return "FD_ERR_WORKSPACE_TOO_SMALL";
+    case FD_ERR_HIP: return "FD_ERR_HIP";
+    }
+    return "FD_UNKNOWN_STATUS";
+}

@@ -1,0 +1,143 @@
+// fd_device.h -- gfx950 device helpers: 16-byte KV loads, storage-type
+// unpacking, wave64 cross-lane reductions, output rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+
+// ---------------------------------------------------------------------------
+// storage types: a 16-byte load holds E elements
+// ---------------------------------------------------------------------------
+template <int DT> struct Storage;
+template <> struct Storage<F32> { static constexpr int E = 4; static constexpr int bytes = 4; };
+template <> struct Storage<F16> { static constexpr int E = 8; static constexpr int bytes = 2; };
+template <> struct Storage<BF16> { static constexpr int E = 8; static constexpr int bytes = 2; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h16) {
+    _Float16 h;
+    uint16_t bits = (uint16_t)h16;
+    __builtin_memcpy(&h, &bits, 2);
+    return (float)h;
+}
+
+// Widen the 16 bytes in `raw` to E fp32 values.
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4 &raw, float *out) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (DT == F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+    } else if constexpr (DT == BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = bf16_lo(w[i]);
+            out[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = f16_bits_to_float(w[i] & 0xffffu);
+            out[2 * i + 1] = f16_bits_to_float(w[i] >> 16);
+        }
+    }
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load of streamed (read-once) data, with the non-temporal hint.
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions inside aligned lane groups of W (W | 64)
+// ---------------------------------------------------------------------------
+// DPP row-local permutations (16-lane rows): quad_perm xor1 / xor2,
+// row_half_mirror (i <-> 7 - i), row_mirror (i <-> 15 - i).  After xor1 and
+// xor2 every lane of a quad holds the quad's value, so the mirrors complete an
+// 8- and a 16-lane butterfly.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "W");
+    if constexpr (W >= 2) v += dpp<kDppXor1>(v);
+    if constexpr (W >= 4) v += dpp<kDppXor2>(v);
+    if constexpr (W >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (W >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (W >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+    if constexpr (W >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if constexpr (W >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if constexpr (W >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(a - b) with the convention that an absent state (a = -inf) weighs 0,
+// also when b is -inf.
+__device__ __forceinline__ float rescale(float a, float b) {
+    return a == -INFINITY ? 0.0f : exp2_fast(a - b);
+}
+
+// ---------------------------------------------------------------------------
+// output rounding (round to nearest even)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN stays a quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;
+    uint16_t bits;
+    __builtin_memcpy(&bits, &h, 2);
+    return bits;
+}
+
+__device__ __forceinline__ void store_out(void *out, size_t idx, float val, int dt) {
+    if (dt == F32)
+        reinterpret_cast<float *>(out)[idx] = val;
+    else if (dt == BF16)
+        reinterpret_cast<uint16_t *>(out)[idx] = float_to_bf16_bits(val);
+    else
+        reinterpret_cast<uint16_t *>(out)[idx] = float_to_f16_bits(val);
+}
+
+// Number of tokens of request b that the kernels read.
+__device__ __forceinline__ int request_len(const int32_t *seq_lens, int b, int cap, int limit) {
+    int n = seq_lens ? seq_lens[b] : cap;
+    n = n < 0 ? 0 : n;
+    n = n > cap ? cap : n;
+    return n > limit ? limit : n;
+}
+
+}  // namespace fd

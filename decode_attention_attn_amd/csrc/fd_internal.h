@@ -1,0 +1,63 @@
+// fd_internal.h -- launch parameters shared by the host entry points and the
+// gfx950 kernels of the split-KV decode-attention library.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxGroup = 16;       // query heads per KV head
+constexpr int kMaxSplits = 8192;
+constexpr int kMaxSplitSize = 1 << 20;
+// unified max: |lo - phi|, |hi - phi| bound, so exp(s - phi) <= e^64 leaves
+// fp32 headroom for sums of up to 2^20 terms times |v|
+constexpr float kMaxUnifiedRange = 64.f;
+
+enum DType : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Everything a split-partial kernel reads.  Scores are handled in log2
+// units: s2 = scale * log2(e) * <q, k>, so that exp(s - m) = exp2(s2 - m2).
+struct PartialParams {
+    const void *q;              // [B, Hq, d]
+    const void *k;              // contiguous [B, cap, Hkv, d] or paged [P, page, Hkv, d]
+    const void *v;
+    const int32_t *seq_lens;    // [B] or nullptr
+    const int32_t *block_table; // [B, max_blocks] (paged) or nullptr
+    float *part_o;              // [B, Hq, S_max, d]
+    float *part_m;              // [B, Hq, S_max]  natural-log units
+    float *part_l;              // [B, Hq, S_max]
+    uint8_t *flags;             // [B, Hq, S_max] or nullptr
+    int32_t *fallback_count;    // [1] or nullptr
+    int32_t B, Hq, Hkv, G, d;
+    int32_t kv_capacity;        // contiguous: tokens per request row; paged: max_blocks * page
+    int32_t page_size;          // 0 = contiguous
+    int32_t max_blocks;
+    int32_t num_pages;
+    int32_t split, max_splits;
+    float scale_log2;           // scale * log2(e)
+    float phi2, lo2, hi2;       // unified max, log2 units
+    int32_t unified;            // 1 = unified max with fallback
+    int32_t dtype;              // DType of q, k, v
+};
+
+struct CombineParams {
+    const float *part_o, *part_m, *part_l;
+    const int32_t *seq_lens;
+    void *out;                  // [B, Hq, d]
+    float *lse;                 // [B, Hq] or nullptr
+    int32_t B, Hq, d;
+    int32_t split, max_splits;
+    int32_t out_dtype;
+};
+
+// Each launcher checks nothing (the entry points validate) and returns the
+// launch status.
+hipError_t launch_partial_valu(const PartialParams &p, hipStream_t stream);
+hipError_t launch_partial_mfma(const PartialParams &p, hipStream_t stream);
+bool mfma_supports(const PartialParams &p);
+hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+
+}  // namespace fd

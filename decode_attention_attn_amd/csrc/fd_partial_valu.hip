@@ -1,0 +1,327 @@
+// fd_partial_valu.hip -- split-partial kernel on the vector ALUs, every dtype.
+//
+// One workgroup (4 waves) per (request b, KV head, split s) covers the whole
+// GQA group of that KV head, so each K/V row is read from HBM once for all of
+// the group's query heads (handbook page "FlashAttention and inference
+// kernels", exercise 3 and the list of improvements after the paged kernel).
+//
+// Data layout in registers: a cache row (one token of one KV head, d
+// elements) is read as 16-byte pieces by LPR = d / E consecutive lanes (E
+// elements per 16 bytes), so one wave instruction reads RPW = 64 / LPR whole
+// rows.  The dot product of a row with each query head is a per-lane partial
+// sum followed by a butterfly over the LPR lanes (DPP).  Each lane group of
+// LPR lanes keeps its own online-softmax state (m, l, O) over the rows it
+// reads; the states are merged at the end of the split, first across the lane
+// groups of a wave and then across the four waves through LDS, by the same
+// max-rescale rule the combine kernel uses.
+//
+// Softmax inside a split:
+//   SYNC -- the FlashAttention recurrence with a running maximum, applied once
+//     per R rows (page "FlashAttention and inference kernels", section
+//     "FlashAttention: tiling plus online softmax").
+//   UNIFIED -- p = exp(s - phi) with the fixed constant phi and plain sums, no
+//     maximum at all (page "FlashDecoding++: Faster Large Language Model
+//     Inference on GPUs", "Asynchronized Softmax with Unified Max Value",
+//     Eq. 3 and Eq. 4).  Every valid score is checked against [lo, hi]; if any
+//     query head of the group saw a score outside it, the workgroup rescans
+//     the split with SYNC and replaces the partials of exactly the flagged
+//     heads ("The Overflow Fallback: Recomputation").
+#include "fd_device.h"
+
+namespace fd {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <int DT, int D, int GMAX>
+struct Cfg {
+    static constexpr int E = Storage<DT>::E;
+    static constexpr int LPR = D / E;                // lanes per cache row
+    static constexpr int RPW = 64 / LPR;             // rows per wave instruction
+    static constexpr int R = GMAX >= 8 ? 2 : 4;      // rows per lane per step
+    static constexpr int TOK_STEP = kWaves * RPW * R;
+    static constexpr int BYTES = Storage<DT>::bytes;
+};
+
+template <int DT, int D, int GMAX>
+struct State {
+    static constexpr int E = Cfg<DT, D, GMAX>::E;
+    float m[GMAX], l[GMAX], acc[GMAX][E];
+    bool bad[GMAX];
+    __device__ void init(float m0) {
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            m[g] = m0;
+            l[g] = 0.f;
+            bad[g] = false;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+        }
+    }
+};
+
+// Element offset of (token t, dim 0) of KV head kvh of request b; ok is
+// cleared when a paged entry points outside the pool.
+template <bool PAGED, int D>
+__device__ __forceinline__ size_t row_offset(const PartialParams &p, int b, int kvh, int t, bool &ok) {
+    size_t row;
+    if constexpr (PAGED) {
+        const int phys = p.block_table[(size_t)b * p.max_blocks + t / p.page_size];
+        ok = ok && phys >= 0 && phys < p.num_pages;
+        row = ((size_t)(ok ? phys : 0) * p.page_size + t % p.page_size) * p.Hkv + kvh;
+    } else {
+        row = ((size_t)b * p.kv_capacity + t) * p.Hkv + kvh;
+    }
+    return row * D;
+}
+
+template <int DT, int D, int GMAX, bool PAGED, bool UNIFIED>
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1,
+                           const float (&qv)[GMAX][Cfg<DT, D, GMAX>::E], State<DT, D, GMAX> &st) {
+    using C = Cfg<DT, D, GMAX>;
+    constexpr int E = C::E, LPR = C::LPR, RPW = C::RPW, R = C::R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = lane / LPR, c = lane % LPR;
+    const char *kb = static_cast<const char *>(p.k);
+    const char *vb = static_cast<const char *>(p.v);
+
+    for (int tb = t0; tb < t1; tb += C::TOK_STEP) {
+        uint4 kr[R], vr[R];
+        bool ok[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int t = tb + (wave * R + r) * RPW + rg;
+            ok[r] = t < t1;
+            const size_t off = (row_offset<PAGED, D>(p, b, kvh, ok[r] ? t : t0, ok[r]) + (size_t)c * E) * C::BYTES;
+            kr[r] = ok[r] ? load16_stream(kb + off) : make_uint4(0, 0, 0, 0);
+            vr[r] = ok[r] ? load16_stream(vb + off) : make_uint4(0, 0, 0, 0);
+        }
+        float s[R][GMAX];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float kf[E];
+            unpack<DT>(kr[r], kf);
+#pragma unroll
+            for (int g = 0; g < GMAX; ++g) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) dot = fmaf(qv[g][e], kf[e], dot);
+                dot = group_sum<LPR>(dot);
+                s[r][g] = ok[r] ? dot * p.scale_log2 : -INFINITY;
+            }
+        }
+        float vf[R][E];
+#pragma unroll
+        for (int r = 0; r < R; ++r) unpack<DT>(vr[r], vf[r]);
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            float mref;
+            if constexpr (UNIFIED) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    st.bad[g] = st.bad[g] || (ok[r] && (s[r][g] < p.lo2 || s[r][g] > p.hi2));
+                mref = p.phi2;
+            } else {
+                float mt = s[0][g];
+#pragma unroll
+                for (int r = 1; r < R; ++r) mt = fmaxf(mt, s[r][g]);
+                const float mn = fmaxf(st.m[g], mt);
+                const float corr = rescale(st.m[g], mn);
+                st.l[g] *= corr;
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.acc[g][e] *= corr;
+                st.m[g] = mn;
+                mref = mn;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float pr = mref == -INFINITY ? 0.f : exp2_fast(s[r][g] - mref);
+                st.l[g] += pr;
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.acc[g][e] = fmaf(pr, vf[r][e], st.acc[g][e]);
+            }
+        }
+    }
+}
+
+// Merge the lane groups of each wave: butterfly over lanes with equal chunk.
+template <int DT, int D, int GMAX>
+__device__ void merge_wave(State<DT, D, GMAX> &st) {
+    using C = Cfg<DT, D, GMAX>;
+#pragma unroll
+    for (int off = C::LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            const float mp = __shfl_xor(st.m[g], off);
+            const float lp = __shfl_xor(st.l[g], off);
+            const float mn = fmaxf(st.m[g], mp);
+            const float a = rescale(st.m[g], mn), bb = rescale(mp, mn);
+            st.l[g] = st.l[g] * a + lp * bb;
+#pragma unroll
+            for (int e = 0; e < C::E; ++e) {
+                const float ap = __shfl_xor(st.acc[g][e], off);
+                st.acc[g][e] = st.acc[g][e] * a + ap * bb;
+            }
+            st.m[g] = mn;
+        }
+    }
+}
+
+template <int D, int GMAX>
+struct Smem {
+    float m[kWaves][GMAX];
+    float l[kWaves][GMAX];
+    float acc[kWaves][GMAX][D];
+    uint32_t bad[kWaves];
+};
+
+// Wave states -> LDS -> the split's partial for the heads in `write_mask`.
+template <int DT, int D, int GMAX>
+__device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Smem<D, GMAX> &sm,
+                             size_t slot0, uint32_t write_mask) {
+    using C = Cfg<DT, D, GMAX>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    merge_wave(st);
+    if (lane < C::LPR) {
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+#pragma unroll
+            for (int e = 0; e < C::E; ++e) sm.acc[wave][g][lane * C::E + e] = st.acc[g][e];
+            if (lane == 0) {
+                sm.m[wave][g] = st.m[g];
+                sm.l[wave][g] = st.l[g];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < p.G * D; idx += kThreads) {
+        const int g = idx / D, dim = idx % D;
+        if (!((write_mask >> g) & 1u)) continue;
+        float mm = sm.m[0][g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, sm.m[w][g]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = rescale(sm.m[w][g], mm);
+            L += sm.l[w][g] * f;
+            A += sm.acc[w][g][dim] * f;
+        }
+        const size_t slot = slot0 + (size_t)g * p.max_splits;
+        p.part_o[slot * D + dim] = L > 0.f ? A / L : 0.f;
+        if (dim == 0) {
+            p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
+            p.part_l[slot] = L;
+        }
+    }
+}
+
+template <int DT, int D, int GMAX, bool PAGED>
+__global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
+    using C = Cfg<DT, D, GMAX>;
+    constexpr int E = C::E;
+    __shared__ Smem<D, GMAX> sm;
+
+    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int G = p.G, h0 = kvh * G;
+    const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
+    const int t0 = s * p.split;
+    const int t1 = min(t0 + p.split, len);
+    const size_t slot0 = ((size_t)b * p.Hq + h0) * p.max_splits + s;
+
+    if (t0 >= t1) {   // empty split: nothing to read
+        if (threadIdx.x < G) {
+            const size_t slot = slot0 + (size_t)threadIdx.x * p.max_splits;
+            p.part_m[slot] = -INFINITY;
+            p.part_l[slot] = 0.f;
+            if (p.flags) p.flags[slot] = 0;
+        }
+        return;
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane % C::LPR;
+    float qv[GMAX][E];
+    const char *qb = static_cast<const char *>(p.q);
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+            const size_t off = (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * C::BYTES;
+            unpack<DT>(load16(qb + off), qv[g]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) qv[g][e] = 0.f;
+        }
+    }
+
+    const uint32_t all = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
+    State<DT, D, GMAX> st;
+    uint32_t badmask = 0;
+    if (p.unified) {
+        st.init(p.phi2);
+        scan_split<DT, D, GMAX, PAGED, true>(p, b, kvh, t0, t1, qv, st);
+        uint32_t mine = 0;
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g)
+            if (__any(st.bad[g])) mine |= 1u << g;
+        if (lane == 0) sm.bad[wave] = mine;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) badmask |= sm.bad[w];
+        badmask &= all;
+        finish_split<DT, D, GMAX>(p, st, sm, slot0, all & ~badmask);
+        if (badmask) {   // synchronized recompute of the flagged heads
+            __syncthreads();
+            st.init(-INFINITY);
+            scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, qv, st);
+            finish_split<DT, D, GMAX>(p, st, sm, slot0, badmask);
+        }
+        if (threadIdx.x == 0 && badmask && p.fallback_count)
+            atomicAdd(p.fallback_count, __builtin_popcount(badmask));
+    } else {
+        st.init(-INFINITY);
+        scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, qv, st);
+        finish_split<DT, D, GMAX>(p, st, sm, slot0, all);
+    }
+    if (p.flags && threadIdx.x < G)
+        p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
+}
+
+template <int DT, int D, int GMAX, bool PAGED>
+hipError_t launch(const PartialParams &p, hipStream_t stream) {
+    dim3 grid(p.max_splits, p.Hkv, p.B);
+    hipLaunchKernelGGL((partial_valu_kernel<DT, D, GMAX, PAGED>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int DT, int D, int GMAX>
+hipError_t by_paged(const PartialParams &p, hipStream_t s) {
+    return p.page_size ? launch<DT, D, GMAX, true>(p, s) : launch<DT, D, GMAX, false>(p, s);
+}
+
+template <int DT, int D>
+hipError_t by_group(const PartialParams &p, hipStream_t s) {
+    if (p.G <= 1) return by_paged<DT, D, 1>(p, s);
+    if (p.G <= 2) return by_paged<DT, D, 2>(p, s);
+    if (p.G <= 4) return by_paged<DT, D, 4>(p, s);
+    if (p.G <= 8) return by_paged<DT, D, 8>(p, s);
+    return by_paged<DT, D, 16>(p, s);
+}
+
+template <int DT>
+hipError_t by_dim(const PartialParams &p, hipStream_t s) {
+    return p.d == 64 ? by_group<DT, 64>(p, s) : by_group<DT, 128>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_partial_valu(const PartialParams &p, hipStream_t stream) {
+    switch (p.dtype) {
+    case F32: return by_dim<F32>(p, stream);
+    case F16: return by_dim<F16>(p, stream);
+    default: return by_dim<BF16>(p, stream);
+    }
+}
+
+}  // namespace fd

@@ -1,0 +1,168 @@
+/*
+ * fd_decode_attn.h -- C ABI of the split-KV decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact single-query attention o = softmax(q K^T / sqrt(d)) V
+ * over a long KV cache (page "Flash-Decoding: Mathematical Foundations, Split-KV
+ * Parallelism, Online Softmax Reduction, and Serving Latency Optimization",
+ * section "The Single-Token Generation Bottleneck"), parallelised along the KV
+ * sequence: each split of `split_size` tokens yields partials (m, l, O)
+ * (same page, "Mathematical Formulation of Split-KV Parallelism") that a second
+ * kernel merges exactly by log-sum-exp ("The Rescaling and Online Softmax
+ * Reduction Algorithm"; the two launches follow "Hardware Execution Topology
+ * and Memory Traffic").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises; it enqueues kernels on
+ *    `stream` (a hipStream_t; NULL = the null stream) and returns a status.
+ *    Device faults (for instance from a table entry the caller got wrong) show
+ *    up at the caller's next synchronisation, not in the status.
+ *  - Tensors are dense, row-major, with 16-byte aligned base pointers; offsets
+ *    are computed in 64 bits.
+ *  - q has shape [B, Hq, d] and the same element type as the cache.
+ *  - GQA: query head h reads KV head h / (Hq / Hkv); consecutive query heads
+ *    share a KV head (page "FlashAttention and inference kernels", section
+ *    "A paged decode attention kernel (with GQA)").  Hq must be a multiple
+ *    of Hkv, and Hq / Hkv <= 16.
+ *  - d is 64 or 128.
+ *  - seq_lens (int32 [B], device) gives each request's number of tokens; NULL
+ *    means every request holds `kv_capacity` tokens.  Negative lengths count
+ *    as 0; lengths beyond the cache or beyond max_splits * split_size are
+ *    clamped to what fits.
+ *  - Split s of request b covers tokens [s * split_size, min((s+1) * split_size,
+ *    len_b)); the last split holds the remainder.  A split with no tokens
+ *    reports m = -inf, l = 0 and leaves its O row unwritten.
+ *  - Partials (fp32): part_o [B, Hq, max_splits, d] holds the split's output
+ *    already divided by its l; part_m, part_l [B, Hq, max_splits] hold the
+ *    split's scaling constant m (natural-log units of scaled scores) and
+ *    l = sum_t exp(s_t - m).
+ *  - lse (fp32 [B, Hq]) = ln sum_t exp(s_t) with s_t = scale * <q, k_t>;
+ *    -inf for an empty request, whose out row is 0.
+ *  - Results are bitwise repeatable run to run (no floating-point atomics).
+ *  - Errors are returned, never thrown; on error nothing is enqueued.
+ */
+#ifndef FD_DECODE_ATTN_H
+#define FD_DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = 1,          /* a NULL where a tensor is required, a bad size or range */
+    FD_ERR_UNSUPPORTED = 2,          /* a valid request this build has no kernel for */
+    FD_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < fd_workspace_bytes(desc) */
+    FD_ERR_HIP = 4                   /* the HIP runtime rejected a launch */
+} fd_status;
+
+typedef enum fd_dtype { FD_F32 = 0, FD_F16 = 1, FD_BF16 = 2 } fd_dtype;
+
+/* Softmax scaling inside a split.
+ * SYNC: each split tracks its own running maximum (the FlashAttention online
+ *   recurrence, page "FlashAttention and inference kernels", section
+ *   "FlashAttention: tiling plus online softmax").
+ * UNIFIED_MAX: every split scales by the same constant phi and keeps plain
+ *   numerator / denominator sums; a split holding a score outside [lo, hi] is
+ *   flagged and recomputed with SYNC (page "FlashDecoding++: Faster Large
+ *   Language Model Inference on GPUs", section "Asynchronized Softmax with
+ *   Unified Max Value", Eq. 3 and 4, "The Overflow Fallback: Recomputation"). */
+typedef enum fd_softmax_mode { FD_SOFTMAX_SYNC = 0, FD_SOFTMAX_UNIFIED_MAX = 1 } fd_softmax_mode;
+
+/* Which split-partial kernel runs.  Every choice computes the same result to
+ * within floating-point rounding. */
+typedef enum fd_kernel {
+    FD_KERNEL_AUTO = 0,  /* the fastest kernel for the shape */
+    FD_KERNEL_VALU = 1,  /* vector-ALU dot products; every dtype */
+    FD_KERNEL_MFMA = 2   /* matrix-core q-group x K^T; f16 / bf16 only */
+} fd_kernel;
+
+typedef struct fd_decode_desc {
+    int32_t B, Hq, Hkv, d;   /* batch, query heads, KV heads, head dimension */
+    int32_t kv_dtype;        /* fd_dtype of q, K and V */
+    int32_t out_dtype;       /* fd_dtype of out */
+    int32_t split_size;      /* tokens per split, 1..2^20; a multiple of page_size when paged */
+    int32_t max_splits;      /* S_max, the split extent of the partial buffers, 1..8192;
+                                max_splits * split_size < 2^31 */
+    float scale;             /* score = scale * <q, k>; <= 0 selects 1 / sqrt(d) */
+    int32_t mode;            /* fd_softmax_mode */
+    float phi, lo, hi;       /* UNIFIED_MAX: p = exp(s - phi); flag when s < lo or s > hi.
+                                Requires lo <= hi, all finite, |lo - phi| <= 64 and
+                                |hi - phi| <= 64, so that exp(s - phi) of an in-range
+                                score and its sums stay finite, normal fp32 numbers. */
+    int32_t kernel;          /* fd_kernel */
+} fd_decode_desc;
+
+/* Split-partial kernel over a contiguous cache.
+ *   k, v          : [B, kv_capacity, Hkv, d] of kv_dtype
+ *   part_o/m/l    : as in the conventions above (written for every split < max_splits)
+ *   flags         : uint8 [B, Hq, max_splits] or NULL; UNIFIED_MAX writes 1 for a
+ *                   (request, query head, split) whose scores left [lo, hi], else 0
+ *   fallback_count: int32 [1] or NULL; UNIFIED_MAX adds the number of flagged
+ *                   (request, query head, split) triples (set it to 0 first for
+ *                   a per-call count)
+ * Splits follow the Flash-Decoding page, "Mathematical Formulation of Split-KV
+ * Parallelism". */
+fd_status fd_decode_attn_partial(const fd_decode_desc *desc, const void *q, const void *k,
+                                 const void *v, int32_t kv_capacity, const int32_t *seq_lens,
+                                 float *part_o, float *part_m, float *part_l, uint8_t *flags,
+                                 int32_t *fallback_count, void *stream);
+
+/* Exact merge of the partials of every (request, query head):
+ * m = max_s m_s, w_s = l_s exp(m_s - m) over splits with l_s > 0, l = sum w_s,
+ * out = sum_s w_s O_s / l, lse = m + ln l (Flash-Decoding page, "The Rescaling
+ * and Online Softmax Reduction Algorithm"; empty splits skipped as in the
+ * handbook's split-K merge exercise).  Request b reads splits
+ * s < ceil(len_b / split_size) (all max_splits when seq_lens is NULL; then
+ * kv_capacity is unused).  out: [B, Hq, d] of out_dtype; lse: fp32 [B, Hq] or NULL. */
+fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float *part_o, const float *part_m,
+                                 const float *part_l, const int32_t *seq_lens, void *out, float *lse,
+                                 void *stream);
+
+/* Partial + combine over a paged cache (page "FlashAttention and inference
+ * kernels", section "PagedAttention": token t of request b lives at slot
+ * t % page_size of physical block block_table[b][t / page_size]).
+ *   k_cache, v_cache : [num_pages, page_size, Hkv, d] of kv_dtype
+ *   block_table      : int32 [B, max_blocks_per_seq]; entries past a request's
+ *                      last page are not read.  An entry outside
+ *                      [0, num_pages) is never dereferenced: its tokens count
+ *                      as absent.
+ *   workspace        : >= fd_workspace_bytes(desc) bytes of device memory, 256-byte
+ *                      aligned; holds part_o, part_m, part_l in that order, each
+ *                      starting on a 256-byte boundary.
+ *   flags, fallback_count : as for fd_decode_attn_partial.
+ * split_size must be a multiple of page_size so that split boundaries fall on
+ * page boundaries (Flash-Decoding page, "Production Implementation Guidelines"). */
+fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q, const void *k_cache,
+                               const void *v_cache, int32_t num_pages, int32_t page_size,
+                               const int32_t *block_table, int32_t max_blocks_per_seq,
+                               const int32_t *seq_lens, void *workspace, size_t workspace_bytes,
+                               void *out, float *lse, uint8_t *flags, int32_t *fallback_count,
+                               void *stream);
+
+/* Bytes of workspace fd_decode_attn_paged needs for `desc` (0 for an invalid desc). */
+size_t fd_workspace_bytes(const fd_decode_desc *desc);
+
+/* Host-only split choice, no GPU call.  Work units W = B * Hkv (one workgroup
+ * covers a GQA group).  With W >= 2 * num_cus no split is needed and the split
+ * is the whole (page-rounded) sequence; otherwise the split gives about
+ * 2 * num_cus work units and is clamped to 128..256 tokens, rounded to whole
+ * pages (Flash-Decoding page, "Production Implementation Guidelines", and
+ * "Mathematical Formulation of Split-KV Parallelism" for S = ceil(N / split)).
+ * page_size 0 means a contiguous cache. */
+fd_status fd_split_heuristic(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                             int32_t num_cus, int32_t *split_size_out, int32_t *num_splits_out);
+
+/* Static, NUL-terminated name of a status. */
+const char *fd_status_string(fd_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_DECODE_ATTN_H */

@@ -77,10 +77,38 @@ def nan_value(dtype: str):
     return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(BF16_QNAN)}[dtype]
 
 
+_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+_CHUNK = 1 << 20
+
+
 def normal(seed: int, shape, dtype: str) -> np.ndarray:
-    """Standard normal draws from PCG64(seed), rounded to `dtype` storage."""
+    """Standard normal draws from PCG64(seed), rounded to `dtype` storage.
+
+    Drawn in chunks through reused buffers (one pass over the output, no
+    full-size temporaries); the values are the generator's sequence in order.
+    """
     rng = np.random.Generator(np.random.PCG64(seed))
-    return encode(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+    out = np.empty(shape, dtype=_STORAGE[dtype])
+    flat = out.reshape(-1)
+    n = flat.size
+    buf = np.empty(min(_CHUNK, max(n, 1)), dtype=np.float32)
+    u = buf.view(np.uint32)
+    t = np.empty_like(u)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        rng.standard_normal(out=buf[:m], dtype=np.float32)
+        if dtype == "bf16":
+            # round to nearest even on the fp32 bits (normal draws are never NaN)
+            tm, um = t[:m], u[:m]
+            np.right_shift(um, 16, out=tm)
+            np.bitwise_and(tm, 1, out=tm)
+            np.add(tm, 0x7FFF, out=tm)
+            np.add(tm, um, out=tm)
+            np.right_shift(tm, 16, out=tm)
+            flat[i:i + m] = tm
+        else:
+            flat[i:i + m] = buf[:m]
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -196,9 +224,8 @@ def make_inputs(w: Workload, poison_tail: bool = True) -> Inputs:
     if w.stress_frac > 0:
         rng = np.random.Generator(np.random.PCG64(SEED_STRESS))
         mask = rng.random(size=shape[:3]) < w.stress_frac
-        kf = decode_f64(k, w.dtype).astype(np.float32)
-        kf[mask] *= np.float32(w.stress_scale)      # exact: power-of-two scaling
-        k = encode(kf, w.dtype)
+        rows = decode_f64(k[mask], w.dtype).astype(np.float32)
+        k[mask] = encode(rows * np.float32(w.stress_scale), w.dtype)   # exact: power-of-two scale
 
     if poison_tail:
         nanv = nan_value(w.dtype)

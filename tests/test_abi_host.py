@@ -1,0 +1,196 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every declared symbol, the split heuristic reproduces the pages'
+rules, and invalid arguments come back as status codes before anything is
+launched.  Every call here either is host-only (the heuristic, the workspace
+size, status names) or fails validation, so no kernel is ever enqueued."""
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+import decode_attention_attn_amd as fd
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "fd_decode_attn.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"fd_decode_attn_partial", "fd_decode_attn_combine", "fd_decode_attn_paged",
+                          "fd_split_heuristic", "fd_workspace_bytes", "fd_status_string"}
+    L = fd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert fd.fd_status_string(fd.FD_OK) == "FD_OK"
+    assert fd.fd_status_string(fd.FD_ERR_WORKSPACE_TOO_SMALL) == "FD_ERR_WORKSPACE_TOO_SMALL"
+    assert fd.fd_status_string(99) == "FD_UNKNOWN_STATUS"
+
+
+def test_desc_struct_matches_header_field_order():
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct fd_decode_desc \{(.*?)\} fd_decode_desc;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        names = decl.split(None, 1)[1]
+        fields += [n.strip() for n in names.split(",")]
+    assert fields == [f[0] for f in fd.fd_decode_desc._fields_]
+
+
+# ----------------------------------------------------------------------------
+# split heuristic: the Flash-Decoding page's dispatch and granularity rules
+# ----------------------------------------------------------------------------
+MI355X_CUS = 256
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,page,split,S", [
+    (1, 8, 8, 512, 0, 128, 4),          # tiny MHA
+    (1, 32, 32, 4096, 0, 256, 16),      # Llama2-7B-shaped MHA
+    (1, 32, 8, 32768, 0, 256, 128),     # long-context GQA
+    (4, 64, 8, 131072, 0, 256, 512),    # unified-max stress shape
+])
+def test_heuristic_reproduces_the_workload_split_sizes(B, Hq, Hkv, N, page, split, S):
+    assert fd.fd_split_heuristic(B, Hq, Hkv, N, page, MI355X_CUS) == (split, S)
+
+
+def test_heuristic_no_split_once_work_fills_the_gpu_twice():
+    # B * Hkv = 512 = 2 * 256 work units: the page's rule says no split
+    split, S = fd.fd_split_heuristic(64, 64, 8, 16384, 16, MI355X_CUS)
+    assert S == 1 and split == 16384
+
+
+def test_heuristic_page_example_split_count(golden):
+    g = golden("flashdecoding_split_sizes.json")["split_count_example"]
+    # the page's example: N = 32768, split 256 -> S = 128; with 16 query heads
+    # at B = 1 that is 2048 blocks (one per query head); here a block covers a
+    # KV head, so use Hq = Hkv = 16
+    split, S = fd.fd_split_heuristic(g["B"], g["query_heads"], g["query_heads"], g["N"], 0, 108)
+    assert split == g["split"] and S == g["S"]
+    assert g["B"] * g["query_heads"] * S == g["blocks"]
+
+
+@pytest.mark.parametrize("page", [1, 16, 32])
+def test_heuristic_is_page_aligned_clamped_and_monotone(golden, page):
+    gran = golden("flashdecoding_split_sizes.json")["split_granularity"]
+    last_S = 0
+    for N in [1, 100, 1000, 4096, 10000, 32768, 100000, 131072]:
+        split, S = fd.fd_split_heuristic(1, 32, 8, N, page, MI355X_CUS)
+        assert split % page == 0
+        assert gran["lo"] <= split <= gran["hi"]
+        assert S == -(-N // split)
+        assert S >= last_S
+        last_S = S
+
+
+def test_heuristic_rejects_bad_arguments():
+    for args in [(0, 8, 8, 100, 0, 256), (1, 8, 3, 100, 0, 256), (1, 8, 8, -1, 0, 256),
+                 (1, 8, 8, 100, -16, 256), (1, 8, 8, 100, 0, 0)]:
+        with pytest.raises(fd.FdError) as e:
+            fd.fd_split_heuristic(*args)
+        assert e.value.status == fd.FD_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------
+# workspace layout
+# ----------------------------------------------------------------------------
+def test_workspace_bytes_layout(golden):
+    d = fd.make_desc(1, 32, 8, 128, "bf16", split_size=256, max_splits=128)
+    rows = 1 * 32 * 128
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert fd.fd_workspace_bytes(d) == r256(rows * 128 * 4) + 2 * r256(rows * 4)
+    # the page's intermediate-buffer example counts 16-bit O; ours is fp32, twice it
+    g = golden("flashdecoding_split_sizes.json")["intermediate_buffer_example"]
+    assert g["B"] * g["H"] * g["S"] * g["d"] * g["elem_bytes"] == g["bytes"]
+    assert r256(rows * 128 * 4) == 2 * g["bytes"]
+
+
+def test_workspace_bytes_zero_for_invalid_desc():
+    assert fd.fd_workspace_bytes(fd.make_desc(1, 6, 4, 128, "bf16", max_splits=4)) == 0
+
+
+# ----------------------------------------------------------------------------
+# validation (every call below fails before any launch)
+# ----------------------------------------------------------------------------
+def _partial_status(desc, kv_capacity=16, with_tensors=False):
+    L = fd.lib()
+    return L.fd_decode_attn_partial(C.byref(desc), None, None, None, kv_capacity, None, None, None, None,
+                                    None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), fd.FD_ERR_INVALID_ARG),               # Hq not a multiple of Hkv
+    (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),              # group of 32 query heads
+    (dict(d=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(split_size=0), fd.FD_ERR_INVALID_ARG),
+    (dict(split_size=(1 << 20) + 1), fd.FD_ERR_INVALID_ARG),
+    (dict(split_size=1 << 20, max_splits=4096), fd.FD_ERR_INVALID_ARG),   # 2^32 tokens
+    (dict(max_splits=0), fd.FD_ERR_INVALID_ARG),
+    (dict(max_splits=8193), fd.FD_ERR_INVALID_ARG),
+    (dict(mode="unified", phi=0.0, lo=1.0, hi=-1.0), fd.FD_ERR_INVALID_ARG),   # lo > hi
+    (dict(mode="unified", phi=-6.0, lo=-6.0, hi=60.0), fd.FD_ERR_INVALID_ARG),  # hi - phi > 64
+    (dict(mode="unified", phi=0.0, lo=-65.0, hi=0.0), fd.FD_ERR_INVALID_ARG),   # phi - lo > 64
+    (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(), fd.FD_ERR_INVALID_ARG),                            # valid desc, NULL tensors
+])
+def test_partial_validation(kw, status):
+    base = dict(B=1, Hq=8, Hkv=8, d=128, kv_dtype="bf16", split_size=256, max_splits=4)
+    base.update(kw)
+    B, Hq, Hkv, d, dt = (base.pop(x) for x in ("B", "Hq", "Hkv", "d", "kv_dtype"))
+    desc = fd.make_desc(B, Hq, Hkv, d, dt, **base)
+    assert _partial_status(desc) == status
+
+
+def test_partial_rejects_bad_enum_codes_and_negative_capacity():
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    desc.kv_dtype = 7
+    assert _partial_status(desc) == fd.FD_ERR_INVALID_ARG
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    desc.mode = 5
+    assert _partial_status(desc) == fd.FD_ERR_INVALID_ARG
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    desc.kernel = 9
+    assert _partial_status(desc) == fd.FD_ERR_INVALID_ARG
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    assert _partial_status(desc, kv_capacity=-1) == fd.FD_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    desc = fd.make_desc(0, 8, 8, 128, "bf16", max_splits=4)
+    assert _partial_status(desc) == fd.FD_OK
+    L = fd.lib()
+    assert L.fd_decode_attn_combine(C.byref(desc), None, None, None, None, None, None, None) == fd.FD_OK
+
+
+def test_paged_validation():
+    L = fd.lib()
+    desc = fd.make_desc(2, 8, 8, 128, "bf16", split_size=100, max_splits=4)
+    # split not a multiple of the page size
+    assert L.fd_decode_attn_paged(C.byref(desc), None, None, None, 10, 16, None, 8, None, None, 0, None, None,
+                                  None, None, None) == fd.FD_ERR_INVALID_ARG
+    desc = fd.make_desc(2, 8, 8, 128, "bf16", split_size=256, max_splits=4)
+    assert L.fd_decode_attn_paged(C.byref(desc), None, None, None, 10, 0, None, 8, None, None, 0, None, None,
+                                  None, None, None) == fd.FD_ERR_INVALID_ARG
+    # NULL tensors
+    assert L.fd_decode_attn_paged(C.byref(desc), None, None, None, 10, 16, None, 8, None, None, 0, None, None,
+                                  None, None, None) == fd.FD_ERR_INVALID_ARG
+
+
+def test_combine_validation():
+    L = fd.lib()
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    assert L.fd_decode_attn_combine(C.byref(desc), None, None, None, None, None, None, None) == \
+        fd.FD_ERR_INVALID_ARG
+    desc.d = 32
+    assert L.fd_decode_attn_combine(C.byref(desc), None, None, None, None, None, None, None) == \
+        fd.FD_ERR_UNSUPPORTED

@@ -1,0 +1,400 @@
+"""GPU parity of the split-KV decode-attention library against the fp64 oracle.
+
+Every case runs the HIP kernels through the C ABI on seeded synth inputs and
+compares element by element with the oracle on the same inputs, at the bar
+stated in fdtest.py.  The five workload shapes run at full size (sampled rows
+for the two multi-GB ones, plus properties checked on every row); smaller
+cases cover the edges: ragged and empty requests, every dtype, head
+dimension and group size, split sizes from 1 token to a single split,
+poisoned cache tails, invalid page entries, and the unified-max fallback.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fdtest as ft
+from fdtest import Run, say
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = ft.torch()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_attn_amd as fd
+    fd.lib()
+
+
+KERNELS = ["valu", "mfma"]
+
+
+def _kernel_ok(kernel, dtype):
+    return kernel == "valu" or dtype in ("f16", "bf16")
+
+
+def _skip_unsupported(fn):
+    """Run fn(); skip the case when the library reports the kernel unsupported."""
+    import decode_attention_attn_amd as fd
+    try:
+        return fn()
+    except fd.FdError as e:
+        if e.status == fd.FD_ERR_UNSUPPORTED:
+            pytest.skip("kernel not available for this shape")
+        raise
+
+
+# ----------------------------------------------------------------------------
+# the handbook's worked exercise, on the GPU
+# ----------------------------------------------------------------------------
+def test_worked_exercise(golden):
+    g = golden("handbook_online_softmax_exercise.json")
+    d, n = 64, 4
+    w = synth.Workload("exercise", B=1, Hq=1, Hkv=1, d=d, dtype="f32", split=2, N=n)
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = math.sqrt(d)        # q.k / sqrt(d) = k0
+    k = np.zeros((1, n, 1, d), np.float32)
+    v = np.zeros((1, n, 1, d), np.float32)
+    k[0, :, 0, 0] = g["scores"]
+    v[0, :, 0, 0] = g["v"]
+    inp = synth.Inputs(w, q, k, v, np.array([n], np.int32))
+    res = Run(inp).run()
+    say(f"exercise: out[0]={res['out'][0, 0]!r}")
+    assert abs(res["out"][0, 0] - g["final"]) <= g["tol"]["final"]
+    ft.check_exact(res, inp, what="exercise")
+    # the two splits are the page's two tiles
+    assert res["part_m"][0].tolist() == [3.0, 5.0]
+    assert abs(res["part_l"][0, 0] - g["tile1"]["l"]) <= g["tol"]["l"]
+    assert abs(res["part_o"][0, 0, 0] * res["part_l"][0, 0] - g["tile1"]["acc"]) <= g["tol"]["acc"]
+
+
+# ----------------------------------------------------------------------------
+# the workload shapes at full size
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_mha", "llama2_7b_mha", "long_gqa_32k"])
+def test_workload_full(name):
+    w = synth.WORKLOADS[name]
+    say(f"[{name}] generating")
+    inp = synth.make_inputs(w)
+    r = Run(inp)
+    res = r.run()
+    e1, e2 = ft.check_exact(res, inp, what=name)
+    ft.check_partials(res, inp, w.split, what=name)
+    say(f"[{name}] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+    # the same kernels without a seq_lens array (every request full length)
+    res2 = r.run(use_lens=False)
+    assert np.array_equal(res2["out"], res["out"]) and np.array_equal(res2["lse"], res["lse"])
+
+
+def test_paged_batched_gqa_full():
+    w = synth.WORKLOADS["paged_batched_gqa"]
+    say("[paged_batched_gqa] generating")
+    inp = synth.make_inputs(w)
+    say(f"[paged_batched_gqa] {inp.k.shape[0]} pages, kv bytes {inp.kv_bytes}")
+    res = Run(inp).run()
+    assert np.isfinite(res["out"]).all() and np.isfinite(res["lse"]).all()
+    rows = ft.sample_rows(w, 256, seed=4)
+    e1, e2 = ft.check_exact(res, inp, rows=rows, what="paged_batched_gqa")
+    ft.check_partials(res, inp, w.split, rows=rows, what="paged_batched_gqa")
+    say(f"[paged_batched_gqa] sampled rows: max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+
+
+def _stress_rate_expectation(inp, c):
+    """Closed-form expected number of flagged (row, split) pairs for bounds [-c, c]."""
+    w = inp.w
+    qf = synth.decode_f64(inp.q, w.dtype)
+    sig = np.linalg.norm(qf, axis=-1).reshape(-1) / math.sqrt(w.d)
+    tail = lambda x: math.erfc(x / math.sqrt(2.0))
+    exp_count = 0.0
+    for s in sig:
+        pt = (1 - w.stress_frac) * tail(c / s) + w.stress_frac * tail(c / (w.stress_scale * s))
+        exp_count += (1 - (1 - pt) ** w.split) * w.max_splits
+    return exp_count
+
+
+def test_umax_stress_full():
+    w = synth.WORKLOADS["umax_stress"]
+    say("[umax_stress] generating")
+    inp = synth.make_inputs(w)
+    r = Run(inp)
+    rows = ft.sample_rows(w, 48, seed=5)
+    sync = r.run()
+    say("[umax_stress] sync done")
+    ft.check_exact(sync, inp, rows=rows, what="umax_stress sync")
+    R, S = w.B * w.Hq, w.max_splits
+    for phi, lo, hi in [(-6.0, -6.0, 6.0), (-20.0, -20.0, 20.0)]:
+        res = r.run(mode="unified", phi=phi, lo=lo, hi=hi)
+        nflag = int(res["flags"].sum())
+        rate = nflag / (R * S)
+        expect = _stress_rate_expectation(inp, hi) / (R * S)
+        say(f"[umax_stress] bounds [{lo}, {hi}] phi={phi}: fallback rate {rate:.4f} (closed form {expect:.4f})")
+        assert set(np.unique(res["flags"])) <= {0, 1}
+        assert res["count"] == nflag
+        assert abs(rate - expect) < 0.05 + 0.1 * expect
+        e1, e2 = ft.check_exact(res, inp, rows=rows, what=f"umax_stress unified {hi}")
+        must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi, rows=rows)
+        got = res["flags"][rows].astype(bool)
+        assert np.all(got[must[rows]]), "a split with a clearly out-of-range score was not flagged"
+        assert not np.any(got[~may[rows]]), "a split with only in-range scores was flagged"
+        # every row: unified and synchronized agree within the bar
+        ft.assert_close(res["out"], sync["out"], w.dtype, "unified vs sync out (all rows)")
+        ft.assert_close(res["lse"], sync["lse"], w.dtype, "unified vs sync lse (all rows)")
+
+
+# ----------------------------------------------------------------------------
+# dtype x head dim x group size x kernel on ragged requests
+# ----------------------------------------------------------------------------
+GROUPS = [(8, 8), (8, 4), (12, 4), (16, 2), (32, 2)]      # G = 1, 2, 3, 8, 16
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", GROUPS)
+def test_shapes(kernel, dtype, d, Hq, Hkv):
+    if not _kernel_ok(kernel, dtype):
+        pytest.skip("mfma kernel is 16-bit only")
+    base = synth.Workload("shape", B=3, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=128, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 1, 385)))
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel))
+    ft.check_exact(res, inp, what=f"{kernel} {dtype} d={d} G={Hq // Hkv}")
+    ft.check_partials(res, inp, 128, what=f"{kernel} {dtype} d={d} G={Hq // Hkv}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("split", [1, 16, 100, 256, 512, 5000])
+def test_split_sizes(kernel, split):
+    base = synth.Workload("splits", B=2, Hq=16, Hkv=4, d=128, dtype="bf16", split=split, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (4096, 777)))
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, split=split))
+    ft.check_exact(res, inp, what=f"split {split}")
+    ft.check_partials(res, inp, split, what=f"split {split}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("page", [0, 16])
+def test_awkward_lengths(kernel, page):
+    lens = (1, 15, 16, 17, 255, 256, 257, 1000, 4096)
+    base = synth.Workload("lens", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=page)
+    inp = synth.make_inputs(synth.with_lens(base, lens))
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel))
+    ft.check_exact(res, inp, what=f"lengths page={page}")
+    ft.check_partials(res, inp, 256, what=f"lengths page={page}")
+
+
+@pytest.mark.parametrize("page", [0, 16])
+def test_empty_request_gives_zero_and_minus_inf(page):
+    base = synth.Workload("empty", B=3, Hq=8, Hkv=2, d=128, dtype="bf16", split=64, N=1, page_size=page)
+    inp = synth.make_inputs(synth.with_lens(base, (0, 100, 0)))
+    res = Run(inp).run()
+    for b in (0, 2):
+        rows = slice(b * 8, (b + 1) * 8)
+        assert np.all(res["out"][rows] == 0.0)
+        assert np.all(res["lse"][rows] == -np.inf)
+    ft.check_exact(res, inp, rows=np.arange(8, 16), what=f"empty page={page}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_token_returns_its_value_row_bitwise(dtype):
+    base = synth.Workload("one", B=2, Hq=8, Hkv=4, d=128, dtype=dtype, split=256, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (1, 1)))
+    res = Run(inp).run()
+    raw = res["raw_out"].reshape(2, 8, 128)
+    for b in range(2):
+        for h in range(8):
+            assert np.array_equal(raw[b, h], inp.v[b, 0, h // 2]), (b, h)
+
+
+def test_equal_scores_give_mean_of_v_and_log_n():
+    base = synth.Workload("q0", B=1, Hq=4, Hkv=1, d=128, dtype="f32", split=256, N=1000)
+    inp = synth.make_inputs(base)
+    inp.q[:] = 0
+    res = Run(inp).run()
+    mean = inp.v[0, :, 0, :].astype(np.float64).mean(axis=0)
+    for h in range(4):
+        ft.assert_close(res["out"][h], mean, "f32", "mean of V")
+        ft.assert_close(res["lse"][h], math.log(1000), "f32", "ln N")
+
+
+def test_identical_value_rows():
+    base = synth.Workload("vrow", B=1, Hq=8, Hkv=2, d=128, dtype="bf16", split=256, N=3000)
+    inp = synth.make_inputs(base)
+    inp.v[:] = inp.v[0, 0]
+    res = Run(inp).run()
+    for h in range(8):
+        want = synth.decode_f64(inp.v[0, 0, h // 4], "bf16")
+        ft.assert_close(res["out"][h], want, "bf16", "identical V rows")
+
+
+def test_out_dtype_can_differ_from_cache_dtype():
+    base = synth.Workload("outf32", B=2, Hq=16, Hkv=4, d=128, dtype="bf16", split=128, N=700)
+    inp = synth.make_inputs(base)
+    res = Run(inp).run(out_dtype="f32")
+    ft.check_exact(res, inp, what="f32 out from bf16 cache")
+
+
+# ----------------------------------------------------------------------------
+# paged indexing: bit-exact
+# ----------------------------------------------------------------------------
+def _relabel_pages(inp, new_table_of):
+    """Same logical data under another physical assignment: returns a new Inputs."""
+    w = inp.w
+    P = inp.k.shape[0]
+    new_table = new_table_of(inp.block_table, P)
+    k = np.empty_like(inp.k)
+    v = np.empty_like(inp.v)
+    valid = inp.block_table >= 0
+    k[new_table[valid]] = inp.k[inp.block_table[valid]]
+    v[new_table[valid]] = inp.v[inp.block_table[valid]]
+    return synth.Inputs(w, inp.q, k, v, inp.seq_lens, new_table)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_paged_permutation_is_bitwise_invariant(kernel):
+    base = synth.Workload("perm", B=4, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=16)
+    inp = synth.make_inputs(synth.with_lens(base, (3000, 17, 1024, 4100)))
+
+    def identity(table, P):
+        t = np.full_like(table, -1)
+        nxt = 0
+        for b in range(table.shape[0]):
+            n = int((table[b] >= 0).sum())
+            t[b, :n] = np.arange(nxt, nxt + n)
+            nxt += n
+        return t
+
+    def reversed_(table, P):
+        t = table.copy()
+        t[table >= 0] = P - 1 - table[table >= 0]
+        return t
+
+    r0 = _skip_unsupported(lambda: Run(inp).run(kernel=kernel))
+    for relabel in (identity, reversed_):
+        r1 = Run(_relabel_pages(inp, relabel)).run(kernel=kernel)
+        for key in ("out", "lse", "part_o", "part_m", "part_l"):
+            a, b = r0[key], r1[key]
+            if key == "part_o":      # O rows of empty splits are unwritten
+                a, b = a[r0["part_l"] > 0], b[r0["part_l"] > 0]
+            assert np.array_equal(a, b), (relabel.__name__, key)
+    ft.check_exact(r0, inp, what="perm")
+
+
+def test_paged_probe_reads_the_page_formula_location():
+    """V rows encode their physical (block, slot) and one key per request is
+    boosted so the softmax is one-hot; the output names the physical row."""
+    base = synth.Workload("probe", B=5, Hq=8, Hkv=2, d=128, dtype="f32", split=64, N=1, page_size=16)
+    inp = synth.make_inputs(synth.with_lens(base, (1, 33, 300, 16, 1000)))
+    w = inp.w
+    P = inp.k.shape[0]
+    inp.k[:] = 0
+    inp.q[:] = 0
+    inp.q[:, :, 0] = 1.0
+    for phys in range(P):
+        for slot in range(16):
+            inp.v[phys, slot, :, 0] = phys
+            inp.v[phys, slot, :, 1] = slot
+    targets = []
+    for b in range(w.B):
+        n = int(inp.seq_lens[b])
+        t_star = (7 * b + 3) % n
+        phys = inp.block_table[b, t_star // 16]
+        inp.k[phys, t_star % 16, :, 0] = 800.0       # score 800 / sqrt(128) ~ 70.7 vs 0
+        targets.append((phys, t_star % 16))
+    res = Run(inp).run()
+    for b, (phys, slot) in enumerate(targets):
+        for h in range(w.Hq):
+            r = b * w.Hq + h
+            assert res["out"][r, 0] == phys and res["out"][r, 1] == slot, (b, h, res["out"][r, :2])
+
+
+def test_invalid_page_entries_are_not_read():
+    """A block-table entry outside the pool makes its 16 tokens absent."""
+    base = synth.Workload("badpage", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", split=64, N=1, page_size=16)
+    inp = synth.make_inputs(synth.with_lens(base, (160, 64)))
+    bad = inp.block_table.copy()
+    bad[0, 3] = -1
+    bad[1, 1] = 10 ** 6
+    binp = synth.Inputs(inp.w, inp.q, inp.k, inp.v, inp.seq_lens, bad)
+    res = Run(binp).run()
+    # expected: the same requests with those pages' tokens removed
+    keep0 = [t for t in range(160) if t // 16 != 3]
+    keep1 = [t for t in range(64) if t // 16 != 1]
+    n = max(len(keep0), len(keep1))
+    wc = synth.Workload("badpage_ref", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", split=64, N=n)
+    kc = np.zeros((2, n, 2, 128), np.uint16)
+    vc = np.zeros_like(kc)
+    for b, keep in enumerate((keep0, keep1)):
+        for i, t in enumerate(keep):
+            kc[b, i] = inp.k[inp.block_table[b, t // 16], t % 16]
+            vc[b, i] = inp.v[inp.block_table[b, t // 16], t % 16]
+    ref_inp = synth.Inputs(wc, inp.q, kc, vc, np.array([len(keep0), len(keep1)], np.int32))
+    ref, lref = ft.oracle_exact(ref_inp)
+    ft.assert_close(res["out"], ref, "bf16", "invalid pages out")
+    ft.assert_close(res["lse"], lref, "bf16", "invalid pages lse")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    base = synth.Workload("repeat", B=2, Hq=64, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=16)
+    inp = synth.make_inputs(synth.with_lens(base, (5000, 2049)))
+    r = Run(inp)
+    a = r.run()
+    b = r.run()
+    for key in ("out", "lse", "part_m", "part_l"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ----------------------------------------------------------------------------
+# unified max value
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("page", [0, 16])
+def test_unified_max_flags_and_fallback(kernel, page):
+    base = synth.Workload("umax", B=2, Hq=32, Hkv=4, d=128, dtype="bf16", split=256, N=1, page_size=page,
+                          stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, (4096, 1500)))
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi))
+    must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may])
+    assert res["count"] == int(got.sum()) and 0 < got.sum() < got.size
+    ft.check_exact(res, inp, what="unified")
+    # partials: unflagged splits use phi, flagged ones their own maximum
+    import oracle
+    p = oracle.problem_of(inp)
+    uo = oracle.unified_max(p, inp.q, inp.k, inp.v, w.split, S, phi, lo, hi, seq_lens=inp.seq_lens,
+                            block_table=inp.block_table)
+    agree = (uo["flags"].astype(bool) == got) & (uo["part_l"] > 0)
+    for key in ("part_m", "part_l", "part_o"):
+        ft.assert_close(res[key][agree], uo[key][agree], "bf16", f"unified {key}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_unified_max_all_flagged_is_bitwise_the_synchronized_path(kernel):
+    base = synth.Workload("umax_all", B=2, Hq=16, Hkv=2, d=128, dtype="bf16", split=128, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 333)))
+    r = Run(inp)
+    sync = _skip_unsupported(lambda: r.run(kernel=kernel))
+    allf = r.run(kernel=kernel, mode="unified", phi=0.0, lo=64.0, hi=64.0)   # every score < lo
+    valid = sync["part_l"] > 0
+    assert np.array_equal(allf["flags"].astype(bool), valid)
+    assert allf["count"] == int(valid.sum())
+    for key in ("out", "lse", "part_m", "part_l"):
+        assert np.array_equal(allf[key], sync[key]), key
+    assert np.array_equal(allf["part_o"][valid], sync["part_o"][valid])
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_unified_max_no_flags_in_a_wide_range(kernel):
+    base = synth.Workload("umax_none", B=2, Hq=16, Hkv=2, d=128, dtype="bf16", split=128, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 333)))
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, mode="unified", phi=-30.0, lo=-30.0, hi=30.0))
+    assert res["count"] == 0 and not res["flags"].any()
+    ft.check_exact(res, inp, what="unified, nothing flagged")
+    valid = res["part_l"] > 0
+    assert np.all(np.abs(res["part_m"][valid] - (-30.0)) < 1e-5)
