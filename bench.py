@@ -1,0 +1,372 @@
+"""Benchmark: split-KV decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole decode-attention pass over one batch: the split-partial
+kernel plus the combine kernel.  The default workload is the long-context
+GQA decode (B=1, Hq=32, Hkv=8, d=128, N=32768, bf16 cache, split 256).
+
+Inputs are generated once (seeded, synthetic), copied to HBM, and replicated
+so that consecutive steps read different copies of the KV cache; the copies
+together exceed the 256 MB Infinity Cache, so every step streams its K and V
+from HBM.  Timing uses HIP events recorded on the stream the kernels are
+launched on (torch's current stream): one pair around the K timed steps
+(nothing else runs in between), then one pair around K back-to-back launches
+of each kernel alone for the per-kernel averages the roofline uses.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py --summarize-profile DIR   writes profile summaries
+        (rocprofv3 kernel-trace stats and PMC counter CSVs under DIR) as
+        markdown tables to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD public spec
+MALL_BYTES = 256 * 2 ** 20        # Infinity Cache
+PARTIAL_KERNEL = "partial"        # substring of the split-partial kernels' names
+COMBINE_KERNEL = "combine_kernel"
+KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/fd_partial_valu.hip",
+                  "decode_attention_attn_amd/csrc/fd_partial_mfma.hip",
+                  "decode_attention_attn_amd/csrc/fd_device.h",
+                  "decode_attention_attn_amd/csrc/fd_combine.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes
+# ----------------------------------------------------------------------------
+def algorithmic_bytes(inp):
+    """Bytes the method must move once: K and V of every (request, KV head,
+    valid token), q, the output, and the block-table entries of the valid pages."""
+    import synth
+    w = inp.w
+    eb = synth.ELEM_BYTES[w.dtype]
+    kv = inp.kv_bytes
+    q = w.B * w.Hq * w.d * eb
+    out = w.B * w.Hq * w.d * eb
+    table = 0
+    if w.page_size:
+        table = int(((inp.seq_lens.astype(np.int64) + w.page_size - 1) // w.page_size).sum()) * 4
+    return dict(kv=kv, q=q, out=out, table=table, partial=kv + q + table, step=kv + q + out + table,
+                units=int(inp.seq_lens.astype(np.int64).sum()) * w.Hkv, per_unit=2 * w.d * eb)
+
+
+# ----------------------------------------------------------------------------
+def run_gpu(args, inp, wl):
+    import torch
+    import decode_attention_attn_amd as fd
+
+    dev = torch.device("cuda:0")
+    w = inp.w
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q = dev_t(inp.q)
+    k0, v0 = dev_t(inp.k), dev_t(inp.v)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    table = torch.from_numpy(inp.block_table).to(dev) if w.page_size else None
+    kv_bytes = k0.numel() * k0.element_size() * 2
+    copies = max(1, math.ceil(4 * MALL_BYTES / kv_bytes)) if not args.warm else 1
+    ks, vs = [k0], [v0]
+    for _ in range(copies - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    log(f"[bench] {w.name}: {copies} KV copies of {kv_bytes / 2**20:.1f} MiB")
+
+    mode = args.mode
+    desc = fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, split_size=w.split, max_seq_len=w.N, mode=mode,
+                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel)
+    S = desc.max_splits
+    out = torch.empty((w.B, w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    flags = torch.zeros((w.B, w.Hq, S), dtype=torch.uint8, device=dev) if mode == "unified" else None
+    count = torch.zeros(1, dtype=torch.int32, device=dev) if mode == "unified" else None
+    L = fd.lib()
+    stream = torch.cuda.current_stream()
+    sp = fd._stream(stream)
+    import ctypes as C
+    dref = C.byref(desc)
+
+    if w.page_size:
+        ws = fd.alloc_workspace(desc, dev)
+        n = w.B * w.Hq * S
+        o_b = (n * w.d * 4 + 255) // 256 * 256
+        m_b = (n * 4 + 255) // 256 * 256
+        fw = ws.view(torch.float32)
+        po = fw[:n * w.d]
+        pm = fw[o_b // 4:o_b // 4 + n]
+        pl = fw[(o_b + m_b) // 4:(o_b + m_b) // 4 + n]
+        # the paged entry point does both kernels; time it as partial, report the split in rocprof
+        calls = []
+        for i in range(copies):
+            calls.append(lambda i=i: fd.fd_decode_attn_paged(desc, q, ks[i], vs[i], w.page_size, table, lens, ws,
+                                                             out, lse, flags, count, stream))
+        combine = None
+    else:
+        po, pm, pl, _ = fd.alloc_partials(desc, dev)
+        # validate the marshalling once through the binding, then call the C entry
+        # points with the same prepared arguments in the timed loop
+        fd.fd_decode_attn_partial(desc, q, ks[0], vs[0], w.N, lens, po, pm, pl, flags, count, stream)
+        fd.fd_decode_attn_combine(desc, po, pm, pl, lens, out, lse, stream)
+        vp = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+        pargs = [(dref, vp(q), vp(ks[i]), vp(vs[i]), C.c_int32(w.N), vp(lens), vp(po), vp(pm), vp(pl), vp(flags),
+                  vp(count), sp) for i in range(copies)]
+        cargs = (dref, vp(po), vp(pm), vp(pl), vp(lens), vp(out), vp(lse), sp)
+        part_fn, comb_fn = L.fd_decode_attn_partial, L.fd_decode_attn_combine
+
+        def check(st, name):
+            if st != 0:
+                raise RuntimeError(f"{name}: {fd.fd_status_string(st)}")
+
+        calls = [lambda i=i: check(part_fn(*pargs[i]), "partial") for i in range(copies)]
+        combine = lambda: check(comb_fn(*cargs), "combine")
+
+    for i in range(args.warmup):
+        calls[i % copies]()
+        if combine:
+            combine()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(body, n):
+        """Average ms of body() over n back-to-back runs, HIP events on `stream`."""
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            body(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def step(i):
+        calls[i % copies]()
+        if combine:
+            combine()
+
+    # the timed steps: K whole steps, nothing else in between
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    step_ms = timed(step, K)
+    t_wall = time.perf_counter() - t_wall
+    # per-kernel averages: K back-to-back launches of each kernel alone
+    part_ms = timed(lambda i: calls[i % copies](), K)
+    comb_ms = timed(lambda i: combine(), K) if combine else 0.0
+    part_us = np.array([part_ms * 1e3])
+    comb_us = np.array([comb_ms * 1e3])
+
+    # one step's result, for the parity spot check
+    calls[0]()
+    if combine:
+        combine()
+    torch.cuda.synchronize()
+    res = dict(out=out.float().cpu().numpy().reshape(-1, w.d).astype(np.float64),
+               lse=lse.cpu().numpy().reshape(-1).astype(np.float64),
+               flags=flags.cpu().numpy() if flags is not None else None)
+    return dict(step_ms=step_ms, wall_ms=t_wall * 1e3 / K, part_us=part_us, comb_us=comb_us, copies=copies,
+                res=res, S=S, device=torch.cuda.get_device_name(0))
+
+
+def parity_spot_check(inp, res, rows):
+    import oracle
+    p = oracle.problem_of(inp)
+    ref, lref = oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table,
+                                 rows=rows)
+    tol = {"f32": (1e-5, 1e-5)}.get(inp.w.dtype, (2e-3, 1e-2))
+    e = np.abs(res["out"][rows] - ref[rows])
+    el = np.abs(res["lse"][rows] - lref[rows])
+    ok = bool(np.all(e <= tol[0] + tol[1] * np.abs(ref[rows])) and np.all(el <= tol[0] + tol[1] * np.abs(lref[rows])))
+    return dict(rows=int(len(rows)), max_abs_err_out=float(e.max()), max_abs_err_lse=float(el.max()), ok=ok)
+
+
+def cpu_baseline(inp, alg, seconds):
+    """The fp64 oracle, as it is, on the host cores: whole decode steps of the
+    same workload repeated until about `seconds` of work have run."""
+    import oracle
+    p = oracle.problem_of(inp)
+    threads = oracle.default_threads()
+    R = inp.w.B * inp.w.Hq
+    # bounded sample: all rows when one step fits the budget, else a prefix of rows
+    t = time.perf_counter()
+    rows = np.arange(min(R, 8), dtype=np.int32)
+    oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table, rows=rows,
+                     threads=threads)
+    per_row = (time.perf_counter() - t) / len(rows)
+    n_rows = int(min(R, max(1, seconds / max(per_row, 1e-9))))
+    rows = np.arange(n_rows, dtype=np.int32)
+    reps = 0
+    t = time.perf_counter()
+    while True:
+        oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table, rows=rows,
+                         threads=threads)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= seconds or reps >= 1000:
+            break
+    step_s = el / reps * (R / n_rows)          # scaled to a whole step
+    return {"value": alg["step"] / step_s / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
+            "us_per_step": step_s * 1e6,
+            "sample": f"{reps} x {n_rows}/{R} (request, query head) rows of the same workload, "
+                      f"{el:.1f} s of fp64 oracle work, scaled to one step"}
+
+
+def traffic_from_profile(workload, kernel_name):
+    """HBM bytes per launch of the partial kernel from the committed PMC summary,
+    if its kernel-source hash matches the current sources; else None."""
+    f = ROOT / "profiles" / f"{workload}_pmc.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("source_hash") != source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel_name)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_gqa_32k")
+    ap.add_argument("--mode", default="sync", choices=["sync", "unified"])
+    ap.add_argument("--phi", type=float, default=-20.0)
+    ap.add_argument("--lo", type=float, default=-20.0)
+    ap.add_argument("--hi", type=float, default=20.0)
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--warm", action="store_true", help="one KV copy (cache-resident for small caches)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profile", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
+              f"MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        return 2
+
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name}")
+    inp = synth.make_inputs(w, poison_tail=False)
+    alg = algorithmic_bytes(inp)
+    g = run_gpu(args, inp, w)
+    part_s = float(np.mean(g["part_us"])) * 1e-6
+    step_s = g["step_ms"] * 1e-3
+    parity = parity_spot_check(inp, g["res"], np.arange(0, w.B * w.Hq, max(1, (w.B * w.Hq) // 32)))
+    log(f"[bench] step {g['step_ms'] * 1e3:.2f} us, partial {np.mean(g['part_us']):.2f} us, "
+        f"combine {np.mean(g['comb_us']):.2f} us (back-to-back averages); parity {parity}")
+    kname = "fd_decode_attn_paged" if w.page_size else PARTIAL_KERNEL
+    traffic = traffic_from_profile(w.name, kname)
+    achieved = alg["partial"] / part_s / 1e9
+    line = {
+        "metric": "decode-attn us/step and achieved HBM TB/s (% of MI355X peak), N=32k GQA",
+        "value": alg["step"] / step_s / 1e12,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": g["step_ms"],
+        "us_per_step": g["step_ms"] * 1e3,
+        "pct_of_hbm_peak": 100.0 * alg["step"] / step_s / 1e9 / HBM_PEAK_GBPS,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N,
+                   "kv_dtype": w.dtype, "split": w.split, "num_splits": g["S"], "page_size": w.page_size,
+                   "softmax": args.mode, "kernel": args.kernel, "kv_copies": g["copies"],
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "kernels_us": {"partial": float(np.mean(g["part_us"])), "combine": float(np.mean(g["comb_us"])),
+                       "timing": "HIP events around K back-to-back launches of each kernel"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg["partial"], "per_unit_bytes": alg["per_unit"],
+                     "units_per_launch": alg["units"]},
+        "parity": parity,
+        "device": g["device"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(inp, alg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0 if parity["ok"] else 1
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 output -> markdown
+# ----------------------------------------------------------------------------
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(d):
+    d = Path(d)
+    for f in sorted(glob.glob(str(d / "**" / "*kernel_stats.csv"), recursive=True)):
+        rows = _read_csv(f)
+        print(f"### kernel stats ({Path(f).name})\n")
+        print("| kernel | calls | avg (us) | min (us) | max (us) | total % |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            name = r.get("Name", "")
+            short = name if len(name) < 90 else name[:87] + "..."
+            print(f"| `{short}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} | "
+                  f"{float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} | "
+                  f"{float(r.get('Percentage', 0)):.1f} |")
+        print()
+    for f in sorted(glob.glob(str(d / "**" / "*counter_collection.csv"), recursive=True)):
+        rows = _read_csv(f)
+        agg = {}
+        for r in rows:
+            key = (r.get("Kernel_Name", ""), r.get("Counter_Name", ""))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+        print(f"### counters ({Path(f).name})\n")
+        print("| kernel | counter | dispatches | mean per dispatch |")
+        print("|---|---|---|---|")
+        for (kn, cn), vals in sorted(agg.items()):
+            short = kn if len(kn) < 90 else kn[:87] + "..."
+            print(f"| `{short}` | {cn} | {len(vals)} | {np.mean(vals):.1f} |")
+        print()
+
+
+if __name__ == "__main__":
+    sys.exit(main())
