@@ -1,11 +1,374 @@
 // fd_partial_mfma.hip -- split-partial kernel with the q-group x K^T product
-// on the matrix cores.  Not built yet: every shape goes to the VALU kernel.
+// on the gfx950 matrix cores (f16 / bf16 caches).
+//
+// Work decomposition (as in the VALU kernel): one workgroup per (request b,
+// KV head, split s) covering all G query heads of that KV head, so K and V are
+// read from HBM once per group (handbook page "FlashAttention and inference
+// kernels", exercise 3).  Each wave walks 16-token blocks of the split.
+//
+// Per block:
+//   K: four 16-byte loads per lane in the natural layout (16 lanes read one
+//      256-byte row, a load covers 4 rows), written to a wave-private LDS tile
+//      with the 16-byte chunk index XOR-swizzled by the row, then read back in
+//      the v_mfma_f32_16x16x32 A-operand layout (lane l: row l % 16, dims
+//      8 * (l / 16) .. + 8 of each 32-dim step), conflict-free.
+//   S^T[token][head] = K q^T: D / 32 MFMAs; the B operand holds q of the group
+//      (heads >= G are zero).  Result lane l: head l % 16, tokens
+//      4 * (l / 16) .. + 3 of the block.
+//   softmax in that layout: SYNC keeps a running per-head maximum across the
+//      wave's blocks (page "FlashAttention and inference kernels", section
+//      "FlashAttention: tiling plus online softmax"); UNIFIED uses the fixed
+//      constant phi and checks every score against [lo, hi] (page
+//      "FlashDecoding++: Faster Large Language Model Inference on GPUs",
+//      Eq. 3 / Eq. 4 and "The Overflow Fallback: Recomputation").
+//   P x V on the vector ALUs in the natural V layout (lane: one row, 8 dims):
+//      the probabilities reach the V lanes through a small LDS buffer.
+// The wave states are merged across lane groups and waves by the max-rescale
+// rule and written as one split partial.
 #include "fd_device.h"
 
 namespace fd {
+namespace {
 
-bool mfma_supports(const PartialParams &) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_partial_mfma(const PartialParams &, hipStream_t) { return hipErrorNotSupported; }
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4 &a, const uint4 &b, f32x4 c) {
+    if constexpr (DT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                     0, 0, 0);
+}
+
+constexpr int kBlk = 16;   // tokens per MFMA block
+
+template <int D, int GMAX, int WAVES>
+struct MCfg {
+    static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
+    static constexpr int LPR = D / 8;                 // lanes per row in the natural layout
+    static constexpr int RPI = 64 / LPR;              // rows per load instruction
+    static constexpr int LI = kBlk / RPI;             // load instructions per block
+    static constexpr int ROWB = D * 2;                // bytes per cache row
+    static constexpr int GP = GMAX <= 2 ? GMAX : ((GMAX + 3) / 4) * 4;   // heads per P row in LDS
+    static constexpr int THREADS = 64 * WAVES;
+};
+
+template <int D, int GMAX, int WAVES>
+struct MSmem {
+    using C = MCfg<D, GMAX, WAVES>;
+    union {
+        struct {
+            uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tile
+            float p[WAVES][kBlk * C::GP];             // probabilities of the block
+            float corr[WAVES][GMAX];                  // running-max rescale factors
+        } loop;
+        struct {
+            float m[WAVES][GMAX];
+            float l[WAVES][GMAX];
+            float acc[WAVES][GMAX][D];
+        } fin;
+    };
+    uint32_t bad[WAVES];
+};
+
+template <int D, int GMAX>
+struct MState {
+    float m, l;          // head l % 16 (MFMA result layout)
+    bool bad;
+    float o[GMAX][8];    // natural V layout: this lane's row group, 8 dims
+    __device__ void init(float m0) {
+        m = m0;
+        l = 0.f;
+        bad = false;
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    }
+};
+
+template <int DT, int D, int GMAX, int WAVES, bool PAGED, bool UNIFIED>
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
+                           MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+    using C = MCfg<D, GMAX, WAVES>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = p.G;
+    const char *kb = static_cast<const char *>(p.k);
+    const char *vb = static_cast<const char *>(p.v);
+    const size_t head_off = (size_t)kvh * D;
+    // a row every lane may read in place of an absent one (its weight is 0)
+    const size_t safe_row = PAGED ? head_off : (((size_t)b * p.kv_capacity + t0) * p.Hkv) * D + head_off;
+
+    const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+    const int rg = lane / C::LPR, ch = lane % C::LPR;           // natural layout coordinates
+    const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
+    char *ktile = reinterpret_cast<char *>(sm.loop.k[wave]);
+
+    for (int blk = wave; blk < nblk; blk += WAVES) {
+        const int tb = t0 + blk * kBlk;
+        // ---- addresses of the block's 16 rows
+        size_t row0;         // element offset of (token tb, kvh, dim 0), rows step by Hkv * D
+        bool page_ok = true;
+        if constexpr (PAGED) {
+            const int phys = p.block_table[(size_t)b * p.max_blocks + tb / p.page_size];
+            page_ok = phys >= 0 && phys < p.num_pages;
+            row0 = (((size_t)(page_ok ? phys : 0) * p.page_size + tb % p.page_size) * p.Hkv) * D + head_off;
+        } else {
+            row0 = (((size_t)b * p.kv_capacity + tb) * p.Hkv) * D + head_off;
+        }
+        const size_t rstride = (size_t)p.Hkv * D;
+
+        // ---- loads: K (swizzled chunks) and V (natural), 16 bytes per lane each
+        uint4 kr[C::LI], vr[C::LI];
+#pragma unroll
+        for (int i = 0; i < C::LI; ++i) {
+            const int r = i * C::RPI + rg;
+            const bool ok = page_ok && tb + r < t1;
+            const size_t row = ok ? row0 + r * rstride : safe_row;
+            const int kch = ch ^ (r & (C::LPR - 1));
+            kr[i] = load16_stream(kb + (row + kch * 8) * 2);
+            vr[i] = load16_stream(vb + (row + ch * 8) * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < C::LI; ++i)
+            *reinterpret_cast<uint4 *>(ktile + i * C::RPI * C::ROWB + lane * 16) = kr[i];
+
+        // ---- S^T = K q^T on the matrix cores
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int slot = (4 * ks + mq) ^ (mrow & (C::LPR - 1));
+            const uint4 a = *reinterpret_cast<const uint4 *>(ktile + mrow * C::ROWB + slot * 16);
+            acc = mfma16x16x32<DT>(a, qop[ks], acc);
+        }
+        float s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = page_ok && tb + 4 * mq + r < t1;
+            s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
+        }
+
+        // ---- softmax for head mrow over these 16 tokens
+        float pr[4];
+        if constexpr (UNIFIED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                st.bad = st.bad || (s[r] != -INFINITY && (s[r] < p.lo2 || s[r] > p.hi2));
+                pr[r] = exp2_fast(s[r] - p.phi2);
+                st.l += pr[r];
+            }
+        } else {
+            float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float mn = fmaxf(st.m, mt);
+            const float corr = rescale(st.m, mn);
+            st.m = mn;
+            st.l *= corr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = mn == -INFINITY ? 0.f : exp2_fast(s[r] - mn);
+                st.l += pr[r];
+            }
+            if (lane < G) sm.loop.corr[wave][lane] = corr;
+        }
+        if (mrow < G) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.loop.p[wave][(4 * mq + r) * C::GP + mrow] = pr[r];
+        }
+        // (LDS operations of one wave execute in order: the reads below see
+        // the writes above, and the next block's writes follow these reads)
+
+        // ---- P x V on the vector ALUs
+        if constexpr (!UNIFIED) {
+            float cf[GMAX];
+            bool any = false;
+#pragma unroll
+            for (int g = 0; g < GMAX; ++g) {
+                cf[g] = g < G ? sm.loop.corr[wave][g] : 1.f;
+                any = any || cf[g] != 1.f;
+            }
+            if (__any(any)) {
+#pragma unroll
+                for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.o[g][e] *= cf[g];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::LI; ++i) {
+            const int r = i * C::RPI + rg;
+            float pv[GMAX];
+#pragma unroll
+            for (int g = 0; g < GMAX; ++g) pv[g] = sm.loop.p[wave][r * C::GP + g];
+            float vf[8];
+            unpack<DT>(vr[i], vf);
+#pragma unroll
+            for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+        }
+    }
+}
+
+// Wave states -> LDS -> the split's partial for the heads in write_mask.
+template <int D, int GMAX, int WAVES>
+__device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
+                             uint32_t write_mask) {
+    using C = MCfg<D, GMAX, WAVES>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // rows of one wave share the running maximum: plain sums across lane groups
+#pragma unroll
+    for (int off = C::LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[g][e] += __shfl_xor(st.o[g][e], off);
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    __syncthreads();   // the fin view aliases the per-wave loop buffers
+    if (lane < C::LPR) {
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.fin.acc[wave][g][lane * 8 + e] = st.o[g][e];
+    }
+    if (lane < GMAX) {
+        sm.fin.m[wave][lane] = st.m;
+        sm.fin.l[wave][lane] = st.l;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < p.G * D; idx += C::THREADS) {
+        const int g = idx / D, dim = idx % D;
+        if (!((write_mask >> g) & 1u)) continue;
+        float mm = sm.fin.m[0][g];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) mm = fmaxf(mm, sm.fin.m[w][g]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float f = rescale(sm.fin.m[w][g], mm);
+            L += sm.fin.l[w][g] * f;
+            A += sm.fin.acc[w][g][dim] * f;
+        }
+        const size_t slot = slot0 + (size_t)g * p.max_splits;
+        p.part_o[slot * D + dim] = L > 0.f ? A / L : 0.f;
+        if (dim == 0) {
+            p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
+            p.part_l[slot] = L;
+        }
+    }
+}
+
+template <int DT, int D, int GMAX, int WAVES, bool PAGED>
+__global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialParams p) {
+    using C = MCfg<D, GMAX, WAVES>;
+    __shared__ MSmem<D, GMAX, WAVES> sm;
+    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int G = p.G, h0 = kvh * G;
+    const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
+    const int t0 = s * p.split;
+    const int t1 = min(t0 + p.split, len);
+    const size_t slot0 = ((size_t)b * p.Hq + h0) * p.max_splits + s;
+
+    if (t0 >= t1) {
+        if (threadIdx.x < G) {
+            const size_t slot = slot0 + (size_t)threadIdx.x * p.max_splits;
+            p.part_m[slot] = -INFINITY;
+            p.part_l[slot] = 0.f;
+            if (p.flags) p.flags[slot] = 0;
+        }
+        return;
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // B operand: q of head (lane % 16) of the group, dims 8 * (lane / 16) of each step
+    uint4 qop[C::KS];
+    {
+        const int g = lane & 15;
+        const char *qb = static_cast<const char *>(p.q);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            qop[ks] = make_uint4(0, 0, 0, 0);
+            if (g < G)
+                qop[ks] = load16(qb + (((size_t)b * p.Hq + h0 + g) * D + 32 * ks + 8 * (lane >> 4)) * 2);
+        }
+    }
+
+    const uint32_t all = (1u << G) - 1u;
+    MState<D, GMAX> st;
+    uint32_t badmask = 0;
+    if (p.unified) {
+        st.init(p.phi2);
+        scan_split<DT, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
+        const uint64_t bal = __ballot(st.bad);
+        const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
+        if (lane == 0) sm.bad[wave] = mine;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
+        badmask &= all;
+        finish_split<D, GMAX, WAVES>(p, st, sm, slot0, all & ~badmask);
+        if (badmask) {   // synchronized recompute of the flagged heads
+            __syncthreads();
+            st.init(-INFINITY);
+            scan_split<DT, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+            finish_split<D, GMAX, WAVES>(p, st, sm, slot0, badmask);
+        }
+        if (threadIdx.x == 0 && badmask && p.fallback_count)
+            atomicAdd(p.fallback_count, __builtin_popcount(badmask));
+    } else {
+        st.init(-INFINITY);
+        scan_split<DT, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+        finish_split<D, GMAX, WAVES>(p, st, sm, slot0, all);
+    }
+    if (p.flags && threadIdx.x < G)
+        p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
+}
+
+constexpr int kWaves = 4;
+
+template <int DT, int D, int GMAX, bool PAGED>
+hipError_t launch(const PartialParams &p, hipStream_t stream) {
+    dim3 grid(p.max_splits, p.Hkv, p.B);
+    hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, kWaves, PAGED>), grid, dim3(64 * kWaves), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int DT, int D, int GMAX>
+hipError_t by_paged(const PartialParams &p, hipStream_t s) {
+    return p.page_size ? launch<DT, D, GMAX, true>(p, s) : launch<DT, D, GMAX, false>(p, s);
+}
+
+template <int DT, int D>
+hipError_t by_group(const PartialParams &p, hipStream_t s) {
+    if (p.G <= 1) return by_paged<DT, D, 1>(p, s);
+    if (p.G <= 2) return by_paged<DT, D, 2>(p, s);
+    if (p.G <= 4) return by_paged<DT, D, 4>(p, s);
+    return by_paged<DT, D, 8>(p, s);
+}
+
+template <int DT>
+hipError_t by_dim(const PartialParams &p, hipStream_t s) {
+    return p.d == 64 ? by_group<DT, 64>(p, s) : by_group<DT, 128>(p, s);
+}
+
+}  // namespace
+
+bool mfma_supports(const PartialParams &p) {
+    if (p.dtype != F16 && p.dtype != BF16) return false;
+    if (p.d != 64 && p.d != 128) return false;
+    if (p.G > 8) return false;                          // register budget of the P x V accumulators
+    if (p.page_size && p.page_size % kBlk) return false;   // a 16-token block must sit in one page
+    return true;
+}
+
+hipError_t launch_partial_mfma(const PartialParams &p, hipStream_t stream) {
+    return p.dtype == F16 ? by_dim<F16>(p, stream) : by_dim<BF16>(p, stream);
+}
 
 }  // namespace fd
