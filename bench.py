@@ -41,6 +41,7 @@ if str(ROOT) not in sys.path:
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 * 2 ** 20        # Infinity Cache
 PARTIAL_KERNEL = "partial"        # substring of the split-partial kernels' names
+COPY_BYTES = 256 * 2 ** 20        # calibration copy: reads and writes this many bytes
 COMBINE_KERNEL = "combine_kernel"
 KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/fd_partial_valu.hip",
                   "decode_attention_attn_amd/csrc/fd_partial_mfma.hip",
@@ -85,6 +86,13 @@ def run_gpu(args, inp, wl):
 
     dev = torch.device("cuda:0")
     w = inp.w
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def dev_t(a):
         a = np.ascontiguousarray(a)
@@ -271,10 +279,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-profile", metavar="DIR")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a device-to-device copy of 256 MiB (a plain copy kernel of known size "
+                         "for scaling HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE runs into profiles/<workload>_pmc.json")
     args = ap.parse_args()
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
+        return 0
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
@@ -366,6 +382,60 @@ def summarize_profile(d):
             short = kn if len(kn) < 90 else kn[:87] + "..."
             print(f"| `{short}` | {cn} | {len(vals)} | {np.mean(vals):.1f} |")
         print()
+
+
+def _counter_rows(d, counter):
+    rows = []
+    for f in glob.glob(str(Path(d) / "**" / "*counter_collection.csv"), recursive=True):
+        rows += [r for r in _read_csv(f) if r.get("Counter_Name") == counter]
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+    return rows
+
+
+def _counter_means(d, counter):
+    """{kernel name: (dispatches, mean counter value per dispatch)} of one --pmc
+    run; the calibration copy is keyed "calibration copy" (the first three
+    copy dispatches, issued before any input upload)."""
+    agg = {}
+    copies = 0
+    for r in _counter_rows(d, counter):
+        name = r.get("Kernel_Name", "")
+        if "copyBuffer" in name:
+            if copies >= 3:
+                continue
+            copies += 1
+            name = "calibration copy"
+        agg.setdefault(name, []).append(float(r.get("Counter_Value", 0)))
+    return {k: (len(v), float(np.mean(v))) for k, v in agg.items()}
+
+
+def pmc_summary(workload, fetch_dir, write_dir):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy of
+    COPY_BYTES.  Writes profiles/<workload>_pmc.json and prints a table."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    copy_name = "calibration copy" if "calibration copy" in fetch else None
+    if copy_name is None:
+        raise SystemExit("no calibration copy kernel in the FETCH_SIZE run (use --copy-calibration)")
+    f_scale = COPY_BYTES / (fetch[copy_name][1] * 1024)
+    w_scale = COPY_BYTES / (write[copy_name][1] * 1024)
+    out = {"workload": workload, "source_hash": source_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    print(f"| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (scaled) |")
+    print("|---|---|---|---|---|")
+    for name in sorted(set(fetch) | set(write)):
+        fk = fetch.get(name, (0, 0.0))
+        wk = write.get(name, (0, 0.0))
+        hbm = fk[1] * 1024 * f_scale + wk[1] * 1024 * w_scale
+        key = PARTIAL_KERNEL if "partial" in name else ("combine" if "combine" in name else name[:60])
+        out["kernels"][key] = {"name": name, "fetch_kib": fk[1], "write_kib": wk[1], "hbm_bytes_per_launch": hbm,
+                               "dispatches": max(fk[0], wk[0])}
+        short = name if len(name) < 80 else name[:77] + "..."
+        print(f"| `{short}` | {max(fk[0], wk[0])} | {fk[1]:.1f} | {wk[1]:.1f} | {hbm:.4g} |")
+    print(f"\ncalibration: copy of {COPY_BYTES} B read as FETCH_SIZE x{f_scale:.4f}, WRITE_SIZE x{w_scale:.4f}")
+    (ROOT / "profiles").mkdir(exist_ok=True)
+    (ROOT / "profiles" / f"{workload}_pmc.json").write_text(json.dumps(out, indent=1) + "\n")
 
 
 if __name__ == "__main__":

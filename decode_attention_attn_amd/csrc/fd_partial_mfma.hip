@@ -91,126 +91,184 @@ struct MState {
     }
 };
 
-template <int DT, int D, int GMAX, int WAVES, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
-                           MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+// Rows of one 16-token block: where they live and whether their page exists.
+struct BlockRows {
+    int tb;          // first token of the block
+    size_t row0;     // element offset of (token tb, kvh, dim 0); rows step by Hkv * d
+    bool page_ok;
+};
+
+template <int D, bool PAGED>
+__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, int b, int kvh, int tb) {
+    BlockRows r;
+    r.tb = tb;
+    r.page_ok = true;
+    const size_t head_off = (size_t)kvh * D;
+    if constexpr (PAGED) {
+        const int phys = p.block_table[(size_t)b * p.max_blocks + tb / p.page_size];
+        r.page_ok = phys >= 0 && phys < p.num_pages;
+        r.row0 = (((size_t)(r.page_ok ? phys : 0) * p.page_size + tb % p.page_size) * p.Hkv) * D + head_off;
+    } else {
+        r.row0 = (((size_t)b * p.kv_capacity + tb) * p.Hkv) * D + head_off;
+    }
+    return r;
+}
+
+// K (chunks XOR-swizzled by row) and V (natural) of a block, 16 bytes per lane each.
+template <int D, int GMAX, int WAVES>
+__device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1, size_t safe_row,
+                                           uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
+                                           uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI]) {
+    using C = MCfg<D, GMAX, WAVES>;
+    const int lane = threadIdx.x & 63;
+    const int rg = lane / C::LPR, ch = lane % C::LPR;
+    const char *kb = static_cast<const char *>(p.k);
+    const char *vb = static_cast<const char *>(p.v);
+    const size_t rstride = (size_t)p.Hkv * D;
+#pragma unroll
+    for (int i = 0; i < C::LI; ++i) {
+        const int r = i * C::RPI + rg;
+        const bool ok = br.page_ok && br.tb + r < t1;
+        const size_t row = ok ? br.row0 + r * rstride : safe_row;
+        const int kch = ch ^ (r & (C::LPR - 1));
+        kr[i] = load16_stream(kb + (row + kch * 8) * 2);
+        vr[i] = load16_stream(vb + (row + ch * 8) * 2);
+    }
+}
+
+template <int DT, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int t1,
+                                              const uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
+                                              const uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI], const uint4 (&qop)[D / 32],
+                                              MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int G = p.G;
-    const char *kb = static_cast<const char *>(p.k);
-    const char *vb = static_cast<const char *>(p.v);
-    const size_t head_off = (size_t)kvh * D;
-    // a row every lane may read in place of an absent one (its weight is 0)
-    const size_t safe_row = PAGED ? head_off : (((size_t)b * p.kv_capacity + t0) * p.Hkv) * D + head_off;
-
-    const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
-    const int rg = lane / C::LPR, ch = lane % C::LPR;           // natural layout coordinates
+    const int rg = lane / C::LPR;
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
     char *ktile = reinterpret_cast<char *>(sm.loop.k[wave]);
-
-    for (int blk = wave; blk < nblk; blk += WAVES) {
-        const int tb = t0 + blk * kBlk;
-        // ---- addresses of the block's 16 rows
-        size_t row0;         // element offset of (token tb, kvh, dim 0), rows step by Hkv * D
-        bool page_ok = true;
-        if constexpr (PAGED) {
-            const int phys = p.block_table[(size_t)b * p.max_blocks + tb / p.page_size];
-            page_ok = phys >= 0 && phys < p.num_pages;
-            row0 = (((size_t)(page_ok ? phys : 0) * p.page_size + tb % p.page_size) * p.Hkv) * D + head_off;
-        } else {
-            row0 = (((size_t)b * p.kv_capacity + tb) * p.Hkv) * D + head_off;
-        }
-        const size_t rstride = (size_t)p.Hkv * D;
-
-        // ---- loads: K (swizzled chunks) and V (natural), 16 bytes per lane each
-        uint4 kr[C::LI], vr[C::LI];
 #pragma unroll
-        for (int i = 0; i < C::LI; ++i) {
-            const int r = i * C::RPI + rg;
-            const bool ok = page_ok && tb + r < t1;
-            const size_t row = ok ? row0 + r * rstride : safe_row;
-            const int kch = ch ^ (r & (C::LPR - 1));
-            kr[i] = load16_stream(kb + (row + kch * 8) * 2);
-            vr[i] = load16_stream(vb + (row + ch * 8) * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < C::LI; ++i)
-            *reinterpret_cast<uint4 *>(ktile + i * C::RPI * C::ROWB + lane * 16) = kr[i];
+    for (int i = 0; i < C::LI; ++i)
+        *reinterpret_cast<uint4 *>(ktile + i * C::RPI * C::ROWB + lane * 16) = kr[i];
 
-        // ---- S^T = K q^T on the matrix cores
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K q^T on the matrix cores
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const int slot = (4 * ks + mq) ^ (mrow & (C::LPR - 1));
-            const uint4 a = *reinterpret_cast<const uint4 *>(ktile + mrow * C::ROWB + slot * 16);
-            acc = mfma16x16x32<DT>(a, qop[ks], acc);
-        }
-        float s[4];
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const int slot = (4 * ks + mq) ^ (mrow & (C::LPR - 1));
+        const uint4 a = *reinterpret_cast<const uint4 *>(ktile + mrow * C::ROWB + slot * 16);
+        acc = mfma16x16x32<DT>(a, qop[ks], acc);
+    }
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = br.page_ok && br.tb + 4 * mq + r < t1;
+        s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
+    }
+
+    // ---- softmax for head mrow over these 16 tokens
+    float pr[4];
+    if constexpr (UNIFIED) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool ok = page_ok && tb + 4 * mq + r < t1;
-            s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
+            st.bad = st.bad || (s[r] != -INFINITY && (s[r] < p.lo2 || s[r] > p.hi2));
+            pr[r] = exp2_fast(s[r] - p.phi2);
+            st.l += pr[r];
         }
+    } else {
+        float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(st.m, mt);
+        const float corr = rescale(st.m, mn);
+        st.m = mn;
+        st.l *= corr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = mn == -INFINITY ? 0.f : exp2_fast(s[r] - mn);
+            st.l += pr[r];
+        }
+        if (lane < G) sm.loop.corr[wave][lane] = corr;
+    }
+    if (mrow < G) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.loop.p[wave][(4 * mq + r) * C::GP + mrow] = pr[r];
+    }
+    // (LDS operations of one wave execute in order: the reads below see the
+    // writes above, and the next block's writes follow these reads)
 
-        // ---- softmax for head mrow over these 16 tokens
-        float pr[4];
-        if constexpr (UNIFIED) {
+    // ---- P x V on the vector ALUs
+    if constexpr (!UNIFIED) {
+        float cf[GMAX];
+        bool any = false;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                st.bad = st.bad || (s[r] != -INFINITY && (s[r] < p.lo2 || s[r] > p.hi2));
-                pr[r] = exp2_fast(s[r] - p.phi2);
-                st.l += pr[r];
-            }
-        } else {
-            float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(st.m, mt);
-            const float corr = rescale(st.m, mn);
-            st.m = mn;
-            st.l *= corr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = mn == -INFINITY ? 0.f : exp2_fast(s[r] - mn);
-                st.l += pr[r];
-            }
-            if (lane < G) sm.loop.corr[wave][lane] = corr;
+        for (int g = 0; g < GMAX; ++g) {
+            cf[g] = g < G ? sm.loop.corr[wave][g] : 1.f;
+            any = any || cf[g] != 1.f;
         }
-        if (mrow < G) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.loop.p[wave][(4 * mq + r) * C::GP + mrow] = pr[r];
-        }
-        // (LDS operations of one wave execute in order: the reads below see
-        // the writes above, and the next block's writes follow these reads)
-
-        // ---- P x V on the vector ALUs
-        if constexpr (!UNIFIED) {
-            float cf[GMAX];
-            bool any = false;
-#pragma unroll
-            for (int g = 0; g < GMAX; ++g) {
-                cf[g] = g < G ? sm.loop.corr[wave][g] : 1.f;
-                any = any || cf[g] != 1.f;
-            }
-            if (__any(any)) {
-#pragma unroll
-                for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st.o[g][e] *= cf[g];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::LI; ++i) {
-            const int r = i * C::RPI + rg;
-            float pv[GMAX];
-#pragma unroll
-            for (int g = 0; g < GMAX; ++g) pv[g] = sm.loop.p[wave][r * C::GP + g];
-            float vf[8];
-            unpack<DT>(vr[i], vf);
+        if (__any(any)) {
 #pragma unroll
             for (int g = 0; g < GMAX; ++g)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+                for (int e = 0; e < 8; ++e) st.o[g][e] *= cf[g];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C::LI; ++i) {
+        const int r = i * C::RPI + rg;
+        float pv[GMAX];
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) pv[g] = sm.loop.p[wave][r * C::GP + g];
+        float vf[8];
+        unpack<DT>(vr[i], vf);
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+    }
+}
+
+// One wave's share of the split: blocks wave, wave + WAVES, ...  With PF the
+// loads of the wave's next block are issued before the current block is
+// computed, so a wave keeps two blocks in flight.
+template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
+                           MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+    using C = MCfg<D, GMAX, WAVES>;
+    const int wave = threadIdx.x >> 6;
+    const size_t head_off = (size_t)kvh * D;
+    // a row every lane may read in place of an absent one (its weight is 0)
+    const size_t safe_row = PAGED ? head_off : (((size_t)b * p.kv_capacity + t0) * p.Hkv) * D + head_off;
+    const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+    if constexpr (PF) {
+        if (wave >= nblk) return;
+        BlockRows cur = block_rows<D, PAGED>(p, b, kvh, t0 + wave * kBlk);
+        uint4 kc[C::LI], vc[C::LI];
+        load_block<D, GMAX, WAVES>(p, cur, t1, safe_row, kc, vc);
+        for (int blk = wave; blk < nblk; blk += WAVES) {
+            const bool more = blk + WAVES < nblk;
+            BlockRows nxt = cur;
+            uint4 kn[C::LI], vn[C::LI];
+            if (more) {
+                nxt = block_rows<D, PAGED>(p, b, kvh, t0 + (blk + WAVES) * kBlk);
+                load_block<D, GMAX, WAVES>(p, nxt, t1, safe_row, kn, vn);
+            }
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, cur, t1, kc, vc, qop, st, sm);
+            if (more) {
+                cur = nxt;
+#pragma unroll
+                for (int i = 0; i < C::LI; ++i) {
+                    kc[i] = kn[i];
+                    vc[i] = vn[i];
+                }
+            }
+        }
+    } else {
+        for (int blk = wave; blk < nblk; blk += WAVES) {
+            const BlockRows br = block_rows<D, PAGED>(p, b, kvh, t0 + blk * kBlk);
+            uint4 kr[C::LI], vr[C::LI];
+            load_block<D, GMAX, WAVES>(p, br, t1, safe_row, kr, vr);
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
         }
     }
 }
@@ -264,7 +322,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     }
 }
 
-template <int DT, int D, int GMAX, int WAVES, bool PAGED>
+template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
 __global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
     __shared__ MSmem<D, GMAX, WAVES> sm;
@@ -304,7 +362,7 @@ __global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialP
     uint32_t badmask = 0;
     if (p.unified) {
         st.init(p.phi2);
-        scan_split<DT, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
+        scan_split<DT, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
         const uint64_t bal = __ballot(st.bad);
         const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
         if (lane == 0) sm.bad[wave] = mine;
@@ -316,27 +374,52 @@ __global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialP
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<DT, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+            scan_split<DT, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
             finish_split<D, GMAX, WAVES>(p, st, sm, slot0, badmask);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<DT, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+        scan_split<DT, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
         finish_split<D, GMAX, WAVES>(p, st, sm, slot0, all);
     }
     if (p.flags && threadIdx.x < G)
         p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
 }
 
-constexpr int kWaves = 4;
+// Launch shape: waves per workgroup and whether a wave prefetches its next
+// block.  Chosen per group size from measurements on MI355X.
+struct Shape {
+    int waves;
+    bool prefetch;
+};
+
+Shape launch_shape(const PartialParams &p) {
+    (void)p;
+    // long-context GQA (G = 4, 1024 workgroups): 2 waves without prefetch
+    // measured 25.4 us against 27.5 (4 waves) and 29.1 (1 wave)
+    return Shape{2, false};
+}
+
+template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
+hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
+    dim3 grid(p.max_splits, p.Hkv, p.B);
+    hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED>), grid, dim3(64 * WAVES), 0, stream, p);
+    return hipGetLastError();
+}
 
 template <int DT, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
-    dim3 grid(p.max_splits, p.Hkv, p.B);
-    hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, kWaves, PAGED>), grid, dim3(64 * kWaves), 0, stream, p);
-    return hipGetLastError();
+    const Shape sh = launch_shape(p);
+    switch (sh.waves * 2 + (sh.prefetch ? 1 : 0)) {
+    case 2: return launch_shaped<DT, D, GMAX, 1, false, PAGED>(p, stream);
+    case 3: return launch_shaped<DT, D, GMAX, 1, true, PAGED>(p, stream);
+    case 4: return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
+    case 5: return launch_shaped<DT, D, GMAX, 2, true, PAGED>(p, stream);
+    case 9: return launch_shaped<DT, D, GMAX, 4, true, PAGED>(p, stream);
+    default: return launch_shaped<DT, D, GMAX, 4, false, PAGED>(p, stream);
+    }
 }
 
 template <int DT, int D, int GMAX>
