@@ -6,29 +6,33 @@
 // (page "Flash-Decoding: Mathematical Foundations, Split-KV Parallelism, ...",
 // section "The Rescaling and Online Softmax Reduction Algorithm", with O_s
 // stored already normalised).  A split with l_s = 0 holds no tokens and is
-// skipped, so its O row is never read (handbook page "FlashAttention and
-// inference kernels", exercise 2).  The weights go to LDS once; each thread
-// then owns four output dimensions of one split group and the groups are
-// summed in a fixed order, so the result is bitwise repeatable.
+// skipped: its O row (never written) gets weight 0 and is never used
+// (handbook page "FlashAttention and inference kernels", exercise 2).  Each
+// thread owns four output dimensions of one split group; the O loads of up
+// to 16 of its splits are issued before the weights are computed so that one
+// memory round trip covers them; the weights go to LDS once and the groups
+// are summed in a fixed order, so the result is bitwise repeatable.
 #include "fd_device.h"
 
 namespace fd {
 namespace {
 
-constexpr int kThreads = 256;
-
+template <int NW>
 __device__ float block_max(float v, float *red) {
     v = group_max<64>(v);
+    if constexpr (NW == 1) return v;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) red[wave] = v;
     __syncthreads();
     v = red[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) v = fmaxf(v, red[w]);
+    for (int w = 1; w < NW; ++w) v = fmaxf(v, red[w]);
     __syncthreads();
     return v;
 }
 
+// (a one-wave block still needs the barrier: it publishes the LDS weights)
+template <int NW>
 __device__ float block_sum(float v, float *red) {
     v = group_sum<64>(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -36,87 +40,144 @@ __device__ float block_sum(float v, float *red) {
     __syncthreads();
     v = red[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) v += red[w];
+    for (int w = 1; w < NW; ++w) v += red[w];
     __syncthreads();
     return v;
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads) combine_kernel(const CombineParams p) {
-    extern __shared__ float sw[];          // [max_splits] split weights
-    constexpr int DQ = D / 4;              // threads per split row (float4 each)
-    constexpr int SG = kThreads / DQ;      // split rows in flight
+// One workgroup of THREADS threads merges DS of the D output dimensions of
+// one (request, query head); gridDim.z = D / DS slices.  No load waits for the
+// request length: O, m and l of all max_splits splits are requested at once
+// (rows past the request's last split are masked afterwards, never used),
+// so one memory round trip covers the inputs.
+template <int D, int DS, int THREADS>
+__global__ void __launch_bounds__(THREADS) combine_kernel(const CombineParams p) {
+    extern __shared__ float sml[];         // [2][max_splits]: m, then l and finally the weights
+    constexpr int DQ = DS / 4;             // threads per split row (float4 each)
+    constexpr int SG = THREADS / DQ;       // split rows covered by one pass of the block
+    constexpr int JC = 16;                 // split rows per thread whose loads are in flight together
+    constexpr int NW = THREADS / 64;
     __shared__ float4 part[SG][DQ];
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[NW];
 
-    const int h = blockIdx.x, b = blockIdx.y;
-    int S = p.max_splits;
+    const int h = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
+    const int Smax = p.max_splits;
+    const size_t row = (size_t)b * p.Hq + h;
+    const size_t base = row * Smax;
+    const float *pm = p.part_m + base, *pl = p.part_l + base;
+    const int dq = threadIdx.x % DQ, sg = threadIdx.x / DQ;
+    const int dim0 = slice * DS + dq * 4;
+    const float *po = p.part_o + base * D + dim0;
+    float *smm = sml, *sww = sml + Smax;
+
+    float4 o[JC];
+#pragma unroll
+    for (int j = 0; j < JC; ++j) {
+        const int s = sg + SG * j;
+        o[j] = s < Smax ? *reinterpret_cast<const float4 *>(po + (size_t)s * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int s = threadIdx.x; s < Smax; s += THREADS) {
+        smm[s] = pm[s];
+        sww[s] = pl[s];
+    }
+    int S = Smax;
     if (p.seq_lens) {
-        const int len = request_len(p.seq_lens, b, p.max_splits * p.split, p.max_splits * p.split);
+        const int len = request_len(p.seq_lens, b, Smax * p.split, Smax * p.split);
         S = (len + p.split - 1) / p.split;
     }
-    const size_t row = (size_t)b * p.Hq + h;
-    const size_t base = row * p.max_splits;
-    const float *pm = p.part_m + base, *pl = p.part_l + base;
 
     float mx = -INFINITY;
-    for (int s = threadIdx.x; s < S; s += kThreads)
-        if (pl[s] > 0.f) mx = fmaxf(mx, pm[s]);
-    mx = block_max(mx, red);
+    for (int s = threadIdx.x; s < S; s += THREADS)
+        if (sww[s] > 0.f) mx = fmaxf(mx, smm[s]);
+    mx = block_max<NW>(mx, red);
 
     float lsum = 0.f;
-    for (int s = threadIdx.x; s < S; s += kThreads) {
-        const float l = pl[s];
-        const float w = l > 0.f ? l * exp2_fast((pm[s] - mx) * kLog2e) : 0.f;
-        sw[s] = w;
+    for (int s = threadIdx.x; s < Smax; s += THREADS) {
+        const float l = sww[s];
+        const float w = (s < S && l > 0.f) ? l * exp2_fast((smm[s] - mx) * kLog2e) : 0.f;
+        sww[s] = w;
         lsum += w;
     }
-    lsum = block_sum(lsum, red);           // its barrier also publishes sw
+    lsum = block_sum<NW>(lsum, red);       // its barrier also publishes the weights
 
-    const int dq = threadIdx.x % DQ, sg = threadIdx.x / DQ;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float *po = p.part_o + base * D + dq * 4;
-    for (int s = sg; s < S; s += SG) {
-        const float w = sw[s];
-        if (w > 0.f) {
-            const float4 o = *reinterpret_cast<const float4 *>(po + (size_t)s * D);
-            a.x = fmaf(w, o.x, a.x);
-            a.y = fmaf(w, o.y, a.y);
-            a.z = fmaf(w, o.z, a.z);
-            a.w = fmaf(w, o.w, a.w);
+    for (int s0 = 0; s0 < S; s0 += SG * JC) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int j = 0; j < JC; ++j) {
+                const int s = s0 + sg + SG * j;
+                o[j] = s < S ? *reinterpret_cast<const float4 *>(po + (size_t)s * D)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < JC; ++j) {
+            const int s = s0 + sg + SG * j;
+            const float w = s < S ? sww[s] : 0.f;
+            if (w > 0.f) {       // a split without tokens has an unwritten O row
+                a.x = fmaf(w, o[j].x, a.x);
+                a.y = fmaf(w, o[j].y, a.y);
+                a.z = fmaf(w, o[j].z, a.z);
+                a.w = fmaf(w, o[j].w, a.w);
+            }
         }
     }
-    part[sg][dq] = a;
-    __syncthreads();
+    if constexpr (SG > 1) {
+        part[sg][dq] = a;
+        __syncthreads();
+    }
     if (sg == 0) {
 #pragma unroll
         for (int j = 1; j < SG; ++j) {
-            const float4 o = part[j][dq];
-            a.x += o.x;
-            a.y += o.y;
-            a.z += o.z;
-            a.w += o.w;
+            const float4 q = part[j][dq];
+            a.x += q.x;
+            a.y += q.y;
+            a.z += q.z;
+            a.w += q.w;
         }
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        const size_t o0 = row * D + dq * 4;
+        const size_t o0 = row * D + dim0;
         store_out(p.out, o0 + 0, a.x * inv, p.out_dtype);
         store_out(p.out, o0 + 1, a.y * inv, p.out_dtype);
         store_out(p.out, o0 + 2, a.z * inv, p.out_dtype);
         store_out(p.out, o0 + 3, a.w * inv, p.out_dtype);
     }
-    if (threadIdx.x == 0 && p.lse) p.lse[row] = lsum > 0.f ? mx + logf(lsum) : -INFINITY;
+    if (threadIdx.x == 0 && slice == 0 && p.lse) p.lse[row] = lsum > 0.f ? mx + logf(lsum) : -INFINITY;
+}
+
+template <int D, int DS, int THREADS>
+hipError_t launch_shaped(const CombineParams &p, hipStream_t stream) {
+    dim3 grid(p.Hq, p.B, D / DS);
+    const size_t smem = 2 * (size_t)p.max_splits * sizeof(float);
+    hipLaunchKernelGGL((combine_kernel<D, DS, THREADS>), grid, dim3(THREADS), smem, stream, p);
+    return hipGetLastError();
+}
+
+// Dimensions per workgroup and threads per workgroup, from measurements on MI355X.
+struct CombineShape {
+    int ds, threads;
+};
+
+CombineShape combine_shape(const CombineParams &p) {
+    (void)p;
+    return CombineShape{128, 256};
+}
+
+template <int D>
+hipError_t launch_d(const CombineParams &p, hipStream_t stream) {
+    const CombineShape c = combine_shape(p);
+    if (c.ds == 32 && c.threads == 64) return launch_shaped<D, 32, 64>(p, stream);
+    if (c.ds == 32 && c.threads == 128) return launch_shaped<D, 32, 128>(p, stream);
+    if (c.ds == 32 && c.threads == 256) return launch_shaped<D, 32, 256>(p, stream);
+    if (c.ds == 64 && c.threads == 128) return launch_shaped<D, 64, 128>(p, stream);
+    if (c.ds == 64 && c.threads == 256) return launch_shaped<D, 64, 256>(p, stream);
+    return launch_shaped<D, D, 256>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream) {
-    dim3 grid(p.Hq, p.B);
-    const size_t smem = (size_t)p.max_splits * sizeof(float);
-    if (p.d == 64)
-        hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kThreads), smem, stream, p);
-    else
-        hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kThreads), smem, stream, p);
-    return hipGetLastError();
+    return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
 }
 
 }  // namespace fd

@@ -60,18 +60,16 @@ struct MCfg {
 template <int D, int GMAX, int WAVES>
 struct MSmem {
     using C = MCfg<D, GMAX, WAVES>;
-    union {
-        struct {
-            uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tile
-            float p[WAVES][kBlk * C::GP];             // probabilities of the block
-            float corr[WAVES][GMAX];                  // running-max rescale factors
-        } loop;
-        struct {
-            float m[WAVES][GMAX];
-            float l[WAVES][GMAX];
-            float acc[WAVES][GMAX][D];
-        } fin;
-    };
+    struct {
+        uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tile
+        float p[WAVES][kBlk * C::GP];             // probabilities of the block
+        float corr[WAVES][GMAX];                  // running-max rescale factors
+    } loop;
+    struct {
+        float4 acc[WAVES][C::RPI][GMAX][D / 4];   // every lane group's unreduced P x V rows
+        float l[WAVES][4][GMAX];                  // every MFMA lane group's partial sums
+        float m[WAVES][GMAX];
+    } fin;
     uint32_t bad[WAVES];
 };
 
@@ -274,48 +272,63 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 }
 
 // Wave states -> LDS -> the split's partial for the heads in write_mask.
+// Every lane stores its unreduced state (P x V rows of its lane group, the
+// partial sum of its MFMA lane group) and, after one barrier, each thread
+// merges one float4 of the output over lane groups and waves by the
+// max-rescale rule.  (All waves of a block share one running maximum, so lane
+// groups add plainly; waves are rescaled to the workgroup maximum.)
 template <int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
                              uint32_t write_mask) {
     using C = MCfg<D, GMAX, WAVES>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // rows of one wave share the running maximum: plain sums across lane groups
+    const int rg = lane / C::LPR, ch = lane % C::LPR;
+    const int mrow = lane & 15, mq = lane >> 4;
 #pragma unroll
-    for (int off = C::LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.o[g][e] += __shfl_xor(st.o[g][e], off);
-    st.l += __shfl_xor(st.l, 16);
-    st.l += __shfl_xor(st.l, 32);
-    __syncthreads();   // the fin view aliases the per-wave loop buffers
-    if (lane < C::LPR) {
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.fin.acc[wave][g][lane * 8 + e] = st.o[g][e];
+    for (int g = 0; g < GMAX; ++g) {
+        sm.fin.acc[wave][rg][g][2 * ch] = make_float4(st.o[g][0], st.o[g][1], st.o[g][2], st.o[g][3]);
+        sm.fin.acc[wave][rg][g][2 * ch + 1] = make_float4(st.o[g][4], st.o[g][5], st.o[g][6], st.o[g][7]);
     }
-    if (lane < GMAX) {
-        sm.fin.m[wave][lane] = st.m;
-        sm.fin.l[wave][lane] = st.l;
+    if (mrow < GMAX) {
+        sm.fin.l[wave][mq][mrow] = st.l;
+        if (mq == 0) sm.fin.m[wave][mrow] = st.m;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < p.G * D; idx += C::THREADS) {
-        const int g = idx / D, dim = idx % D;
+    constexpr int D4 = D / 4;
+    for (int idx = threadIdx.x; idx < p.G * D4; idx += C::THREADS) {
+        const int g = idx / D4, d4 = idx % D4;
         if (!((write_mask >> g) & 1u)) continue;
         float mm = sm.fin.m[0][g];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) mm = fmaxf(mm, sm.fin.m[w][g]);
-        float L = 0.f, A = 0.f;
+        float L = 0.f;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float f = rescale(sm.fin.m[w][g], mm);
-            L += sm.fin.l[w][g] * f;
-            A += sm.fin.acc[w][g][dim] * f;
+            float lw = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lw += sm.fin.l[w][q][g];
+            float4 aw = sm.fin.acc[w][0][g][d4];
+#pragma unroll
+            for (int r = 1; r < C::RPI; ++r) {
+                const float4 x = sm.fin.acc[w][r][g][d4];
+                aw.x += x.x;
+                aw.y += x.y;
+                aw.z += x.z;
+                aw.w += x.w;
+            }
+            L = fmaf(lw, f, L);
+            A.x = fmaf(aw.x, f, A.x);
+            A.y = fmaf(aw.y, f, A.y);
+            A.z = fmaf(aw.z, f, A.z);
+            A.w = fmaf(aw.w, f, A.w);
         }
         const size_t slot = slot0 + (size_t)g * p.max_splits;
-        p.part_o[slot * D + dim] = L > 0.f ? A / L : 0.f;
-        if (dim == 0) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *reinterpret_cast<float4 *>(p.part_o + slot * D + 4 * d4) = make_float4(A.x * inv, A.y * inv, A.z * inv,
+                                                                               A.w * inv);
+        if (d4 == 0) {
             p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
             p.part_l[slot] = L;
         }
@@ -325,6 +338,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
 __global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
+    static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
     const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int G = p.G, h0 = kvh * G;
@@ -412,13 +426,18 @@ hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
 template <int DT, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
     const Shape sh = launch_shape(p);
+    constexpr bool four_fit = sizeof(MSmem<D, GMAX, 4>) <= 65536;
     switch (sh.waves * 2 + (sh.prefetch ? 1 : 0)) {
     case 2: return launch_shaped<DT, D, GMAX, 1, false, PAGED>(p, stream);
     case 3: return launch_shaped<DT, D, GMAX, 1, true, PAGED>(p, stream);
-    case 4: return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
     case 5: return launch_shaped<DT, D, GMAX, 2, true, PAGED>(p, stream);
-    case 9: return launch_shaped<DT, D, GMAX, 4, true, PAGED>(p, stream);
-    default: return launch_shaped<DT, D, GMAX, 4, false, PAGED>(p, stream);
+    case 8:
+        if constexpr (four_fit) return launch_shaped<DT, D, GMAX, 4, false, PAGED>(p, stream);
+        return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
+    case 9:
+        if constexpr (four_fit) return launch_shaped<DT, D, GMAX, 4, true, PAGED>(p, stream);
+        return launch_shaped<DT, D, GMAX, 2, true, PAGED>(p, stream);
+    default: return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
     }
 }
 

@@ -87,7 +87,7 @@ typedef struct fd_decode_desc {
     int32_t kv_dtype;        /* fd_dtype of q, K and V */
     int32_t out_dtype;       /* fd_dtype of out */
     int32_t split_size;      /* tokens per split, 1..2^20; a multiple of page_size when paged */
-    int32_t max_splits;      /* S_max, the split extent of the partial buffers, 1..8192;
+    int32_t max_splits;      /* S_max, the split extent of the partial buffers, 1..4096;
                                 max_splits * split_size < 2^31 */
     float scale;             /* score = scale * <q, k>; <= 0 selects 1 / sqrt(d) */
     int32_t mode;            /* fd_softmax_mode */

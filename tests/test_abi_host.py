@@ -135,8 +135,9 @@ def _partial_status(desc, kv_capacity=16, with_tensors=False):
     (dict(split_size=0), fd.FD_ERR_INVALID_ARG),
     (dict(split_size=(1 << 20) + 1), fd.FD_ERR_INVALID_ARG),
     (dict(split_size=1 << 20, max_splits=4096), fd.FD_ERR_INVALID_ARG),   # 2^32 tokens
+    (dict(split_size=1 << 19, max_splits=4096), fd.FD_ERR_INVALID_ARG),   # 2^31 tokens
     (dict(max_splits=0), fd.FD_ERR_INVALID_ARG),
-    (dict(max_splits=8193), fd.FD_ERR_INVALID_ARG),
+    (dict(max_splits=4097), fd.FD_ERR_INVALID_ARG),
     (dict(mode="unified", phi=0.0, lo=1.0, hi=-1.0), fd.FD_ERR_INVALID_ARG),   # lo > hi
     (dict(mode="unified", phi=-6.0, lo=-6.0, hi=60.0), fd.FD_ERR_INVALID_ARG),  # hi - phi > 64
     (dict(mode="unified", phi=0.0, lo=-65.0, hi=0.0), fd.FD_ERR_INVALID_ARG),   # phi - lo > 64
