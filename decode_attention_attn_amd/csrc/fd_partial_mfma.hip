@@ -96,14 +96,35 @@ struct BlockRows {
     bool page_ok;
 };
 
+// The split's block-table entries, one per lane (pages t0 / page .. + 63),
+// read once per workgroup; blocks beyond them read the table directly.
+struct PageCache {
+    int base;        // first page index held
+    int entry;       // this lane's entry: page base + lane
+};
+
+template <bool PAGED>
+__device__ __forceinline__ PageCache load_pages(const PartialParams &p, int b, int t0, int t1) {
+    PageCache pc{0, -1};
+    if constexpr (PAGED) {
+        const int lane = threadIdx.x & 63;
+        pc.base = t0 / p.page_size;
+        const int last = (t1 - 1) / p.page_size;          // t1 > t0 here
+        if (pc.base + lane <= last) pc.entry = p.block_table[(size_t)b * p.max_blocks + pc.base + lane];
+    }
+    return pc;
+}
+
 template <int D, bool PAGED>
-__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, int b, int kvh, int tb) {
+__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, const PageCache &pc, int b, int kvh, int tb) {
     BlockRows r;
     r.tb = tb;
     r.page_ok = true;
     const size_t head_off = (size_t)kvh * D;
     if constexpr (PAGED) {
-        const int phys = p.block_table[(size_t)b * p.max_blocks + tb / p.page_size];
+        const int pg = tb / p.page_size;                  // wave-uniform
+        const int phys = pg - pc.base < 64 ? __builtin_amdgcn_readlane(pc.entry, pg - pc.base)
+                                           : p.block_table[(size_t)b * p.max_blocks + pg];
         r.page_ok = phys >= 0 && phys < p.num_pages;
         r.row0 = (((size_t)(r.page_ok ? phys : 0) * p.page_size + tb % p.page_size) * p.Hkv) * D + head_off;
     } else {
@@ -228,42 +249,42 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
 
 // One wave's share of the split: blocks wave, wave + WAVES, ...  With PF the
 // loads of the wave's next block are issued before the current block is
-// computed, so a wave keeps two blocks in flight.
+// computed, so a wave keeps two blocks in flight.  Paged caches read the
+// split's block-table entries once (one per lane) and pick each block's page
+// from them with a lane read.
 template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
 __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
                            MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t head_off = (size_t)kvh * D;
     // a row every lane may read in place of an absent one (its weight is 0)
     const size_t safe_row = PAGED ? head_off : (((size_t)b * p.kv_capacity + t0) * p.Hkv) * D + head_off;
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+    const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
     if constexpr (PF) {
+        // ping-pong: block A computes while block B loads, then the roles swap
+        // (unrolled by two so no register copy has to wait on in-flight loads)
         if (wave >= nblk) return;
-        BlockRows cur = block_rows<D, PAGED>(p, b, kvh, t0 + wave * kBlk);
-        uint4 kc[C::LI], vc[C::LI];
-        load_block<D, GMAX, WAVES>(p, cur, t1, safe_row, kc, vc);
-        for (int blk = wave; blk < nblk; blk += WAVES) {
-            const bool more = blk + WAVES < nblk;
-            BlockRows nxt = cur;
-            uint4 kn[C::LI], vn[C::LI];
-            if (more) {
-                nxt = block_rows<D, PAGED>(p, b, kvh, t0 + (blk + WAVES) * kBlk);
-                load_block<D, GMAX, WAVES>(p, nxt, t1, safe_row, kn, vn);
+        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + wave * kBlk), rb = ra;
+        uint4 ka[C::LI], va[C::LI], kb2[C::LI], vb2[C::LI];
+        load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
+        for (int blk = wave; blk < nblk; blk += 2 * WAVES) {
+            const bool has_b = blk + WAVES < nblk;
+            if (has_b) {
+                rb = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + WAVES) * kBlk);
+                load_block<D, GMAX, WAVES>(p, rb, t1, safe_row, kb2, vb2);
             }
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, cur, t1, kc, vc, qop, st, sm);
-            if (more) {
-                cur = nxt;
-#pragma unroll
-                for (int i = 0; i < C::LI; ++i) {
-                    kc[i] = kn[i];
-                    vc[i] = vn[i];
-                }
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            if (blk + 2 * WAVES < nblk) {
+                ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + 2 * WAVES) * kBlk);
+                load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
             }
+            if (has_b) compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
         }
     } else {
         for (int blk = wave; blk < nblk; blk += WAVES) {
-            const BlockRows br = block_rows<D, PAGED>(p, b, kvh, t0 + blk * kBlk);
+            const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk);
             uint4 kr[C::LI], vr[C::LI];
             load_block<D, GMAX, WAVES>(p, br, t1, safe_row, kr, vr);
             compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
@@ -410,9 +431,10 @@ struct Shape {
 };
 
 Shape launch_shape(const PartialParams &p) {
-    (void)p;
     // long-context GQA (G = 4, 1024 workgroups): 2 waves without prefetch
-    // measured 25.4 us against 27.5 (4 waves) and 29.1 (1 wave)
+    // measured 25.4 us against 27.5 (4 waves) and 29.1 (1 wave); groups of 8
+    // (160 VGPRs): 1 wave, 390 us against 433 us (2 waves) on B=4, N=128k
+    if (p.G > 4) return Shape{1, false};
     return Shape{2, false};
 }
 
