@@ -1,5 +1,5 @@
-// fd_partial_mfma.hip -- split-partial kernel with the q-group x K^T product
-// on the gfx950 matrix cores (f16 / bf16 caches).
+// fd_partial_mfma.hip -- split-partial kernel on the gfx950 matrix cores
+// (f16 / bf16 caches).
 //
 // Work decomposition (as in the VALU kernel): one workgroup per (request b,
 // KV head, split s) covering all G query heads of that KV head, so K and V are
@@ -7,24 +7,32 @@
 // kernels", exercise 3).  Each wave walks 16-token blocks of the split.
 //
 // Per block:
-//   K: four 16-byte loads per lane in the natural layout (16 lanes read one
-//      256-byte row, a load covers 4 rows), written to a wave-private LDS tile
-//      with the 16-byte chunk index XOR-swizzled by the row, then read back in
-//      the v_mfma_f32_16x16x32 A-operand layout (lane l: row l % 16, dims
-//      8 * (l / 16) .. + 8 of each 32-dim step), conflict-free.
-//   S^T[token][head] = K q^T: D / 32 MFMAs; the B operand holds q of the group
-//      (heads >= G are zero).  Result lane l: head l % 16, tokens
-//      4 * (l / 16) .. + 3 of the block.
+//   loads: K and V rows with 16-byte non-temporal loads, 16 lanes per 256-byte
+//      row (coalesced), written to wave-private LDS tiles.  The K tile's
+//      16-byte chunks are XOR-swizzled by (row & 15), the V tile's by
+//      2 * (row & 7), so the two operand reads below are bank-conflict-free.
+//   S^T[token][head] = K q^T: D / 32 v_mfma_f32_16x16x32; A = the K tile
+//      (lane l: token l % 16, dims 8 * (l / 16) .. + 8 of each 32-dim step),
+//      B = q of the group (heads >= G zero).  Result lane l: head l % 16,
+//      tokens 4 * (l / 16) .. + 3 of the block.
 //   softmax in that layout: SYNC keeps a running per-head maximum across the
 //      wave's blocks (page "FlashAttention and inference kernels", section
 //      "FlashAttention: tiling plus online softmax"); UNIFIED uses the fixed
 //      constant phi and checks every score against [lo, hi] (page
 //      "FlashDecoding++: Faster Large Language Model Inference on GPUs",
 //      Eq. 3 / Eq. 4 and "The Overflow Fallback: Recomputation").
-//   P x V on the vector ALUs in the natural V layout (lane: one row, 8 dims):
-//      the probabilities reach the V lanes through a small LDS buffer.
-// The wave states are merged across lane groups and waves by the max-rescale
-// rule and written as one split partial.
+//   O[head][dim] += P V: D / 16 slices of v_mfma_f32_16x16x16.  The result
+//      layout of S^T is the A-operand layout of P (head l % 16, tokens
+//      4 * (l / 16) + e), so the probabilities stay in registers; they enter
+//      as a 16-bit high part plus the 16-bit rounding of the fp32 residual
+//      (two MFMAs), which keeps the weights to about 14 bits or better.
+//      B (lane j of lane group q: V[token 4q + k][dim j] of the slice) comes
+//      from the V tile with ds_read_b64_tr_b16, whose result is lane j,
+//      element k = element j % 4 of the 8-byte row addressed by lane 4k + j / 4
+//      of the group.  O lands with heads on rows: 4 registers per slice,
+//      independent of G, and no cross-lane reduction at the end.
+// The wave states are merged across waves by the max-rescale rule and
+// written as one split partial.
 #include "fd_device.h"
 
 namespace fd {
@@ -32,6 +40,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int DT>
@@ -44,16 +54,54 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint4 &a, const uint4 &b, f3
                                                      0, 0, 0);
 }
 
+// O += P V for one 16-dim slice: A = 4 probabilities, B = 4 values (16-bit each)
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x16(const s16x4 &a, const s16x4 &b, f32x4 c) {
+    if constexpr (DT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                    0, 0, 0);
+}
+
+// Four fp32 probabilities -> 16-bit high parts and 16-bit parts of the exact
+// fp32 residuals, packed as MFMA operands.  bf16: the high part is the top
+// 16 bits (truncation); f16: round toward zero.  Either way hi + lo carries
+// the weight to a relative error below 2^-14.
+template <int DT>
+__device__ __forceinline__ void split_probs(const float (&pr)[4], s16x4 &hi, s16x4 &lo) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float a = pr[2 * i], b = pr[2 * i + 1];
+        if constexpr (DT == BF16) {
+            const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+            const float ra = a - __uint_as_float(ua & 0xffff0000u);
+            const float rb = b - __uint_as_float(ub & 0xffff0000u);
+            h[i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);      // [ua.hi16 | ub.hi16 << 16]
+            l[i] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+        } else {
+            const auto hh = __builtin_amdgcn_cvt_pkrtz(a, b);
+            const float ra = a - (float)hh[0], rb = b - (float)hh[1];
+            const auto ll = __builtin_amdgcn_cvt_pkrtz(ra, rb);
+            h[i] = __builtin_bit_cast(uint32_t, hh);
+            l[i] = __builtin_bit_cast(uint32_t, ll);
+        }
+    }
+    hi = __builtin_bit_cast(s16x4, make_uint2(h[0], h[1]));
+    lo = __builtin_bit_cast(s16x4, make_uint2(l[0], l[1]));
+}
+
 constexpr int kBlk = 16;   // tokens per MFMA block
 
 template <int D, int GMAX, int WAVES>
 struct MCfg {
-    static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
+    static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension (QK)
+    static constexpr int SL = D / 16;                 // 16-dim output slices (PV)
     static constexpr int LPR = D / 8;                 // lanes per row in the natural layout
     static constexpr int RPI = 64 / LPR;              // rows per load instruction
     static constexpr int LI = kBlk / RPI;             // load instructions per block
     static constexpr int ROWB = D * 2;                // bytes per cache row
-    static constexpr int GP = GMAX <= 2 ? GMAX : ((GMAX + 3) / 4) * 4;   // heads per P row in LDS
     static constexpr int THREADS = 64 * WAVES;
 };
 
@@ -62,11 +110,11 @@ struct MSmem {
     using C = MCfg<D, GMAX, WAVES>;
     struct {
         uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tile
-        float p[WAVES][kBlk * C::GP];             // probabilities of the block
-        float corr[WAVES][GMAX];                  // running-max rescale factors
+        uint4 v[WAVES][kBlk * C::ROWB / 16];      // wave-private V tile
+        float corr[WAVES][16];                    // running-max rescale factors per head row
     } loop;
     struct {
-        float4 acc[WAVES][C::RPI][GMAX][D / 4];   // every lane group's unreduced P x V rows
+        float acc[WAVES][GMAX][D];                // each wave's P x V rows of the real heads
         float l[WAVES][4][GMAX];                  // every MFMA lane group's partial sums
         float m[WAVES][GMAX];
     } fin;
@@ -75,17 +123,15 @@ struct MSmem {
 
 template <int D, int GMAX>
 struct MState {
-    float m, l;          // head l % 16 (MFMA result layout)
+    float m, l;             // head l % 16 (S^T layout)
     bool bad;
-    float o[GMAX][8];    // natural V layout: this lane's row group, 8 dims
+    f32x4 o[D / 16];        // O[head 4 * (l / 16) + r][16 * slice + l % 16]
     __device__ void init(float m0) {
         m = m0;
         l = 0.f;
         bad = false;
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+        for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 };
 
@@ -162,13 +208,18 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
                                               MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = p.G;
-    const int rg = lane / C::LPR;
+    const int rg = lane / C::LPR, ch = lane % C::LPR;
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
     char *ktile = reinterpret_cast<char *>(sm.loop.k[wave]);
+    char *vtile = reinterpret_cast<char *>(sm.loop.v[wave]);
 #pragma unroll
-    for (int i = 0; i < C::LI; ++i)
+    for (int i = 0; i < C::LI; ++i) {
+        // K chunks arrive pre-swizzled (the load picked chunk ch ^ (row & (LPR-1)));
+        // V chunk ch of row r goes to slot ch ^ (2 * (r & (LPR/2 - 1)))
+        const int r = i * C::RPI + rg;
         *reinterpret_cast<uint4 *>(ktile + i * C::RPI * C::ROWB + lane * 16) = kr[i];
+        *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
+    }
 
     // ---- S^T = K q^T on the matrix cores
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -200,6 +251,7 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = fmaxf(st.m, mt);
         const float corr = rescale(st.m, mn);
+        const bool moved = mn != st.m;
         st.m = mn;
         st.l *= corr;
 #pragma unroll
@@ -207,43 +259,36 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
             pr[r] = mn == -INFINITY ? 0.f : exp2_fast(s[r] - mn);
             st.l += pr[r];
         }
-        if (lane < G) sm.loop.corr[wave][lane] = corr;
-    }
-    if (mrow < G) {
+        // rescale the P x V accumulators (heads on rows 4 * (l / 16) + r)
+        if (__any(moved)) {
+            if (lane < 16) sm.loop.corr[wave][lane] = corr;
+            const float4 cf = *reinterpret_cast<const float4 *>(&sm.loop.corr[wave][4 * mq]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.loop.p[wave][(4 * mq + r) * C::GP + mrow] = pr[r];
+            for (int i = 0; i < C::SL; ++i) {
+                st.o[i][0] *= cf.x;
+                st.o[i][1] *= cf.y;
+                st.o[i][2] *= cf.z;
+                st.o[i][3] *= cf.w;
+            }
+        }
     }
-    // (LDS operations of one wave execute in order: the reads below see the
-    // writes above, and the next block's writes follow these reads)
 
-    // ---- P x V on the vector ALUs
-    if constexpr (!UNIFIED) {
-        float cf[GMAX];
-        bool any = false;
+    // ---- O += P V on the matrix cores
+    s16x4 phi, plo;
+    split_probs<DT>(pr, phi, plo);
+    // this lane's 8-byte row of the transposing read: token 4 * mq + mrow / 4,
+    // dims 16 * slice + 4 * (mrow % 4) .. + 3
+    const int vrow = 4 * mq + (mrow >> 2);
+    const char *vrow_base = vtile + vrow * C::ROWB;
+    const int vsw = 2 * (vrow & (C::LPR / 2 - 1));
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g) {
-            cf[g] = g < G ? sm.loop.corr[wave][g] : 1.f;
-            any = any || cf[g] != 1.f;
-        }
-        if (__any(any)) {
-#pragma unroll
-            for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) st.o[g][e] *= cf[g];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::LI; ++i) {
-        const int r = i * C::RPI + rg;
-        float pv[GMAX];
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g) pv[g] = sm.loop.p[wave][r * C::GP + g];
-        float vf[8];
-        unpack<DT>(vr[i], vf);
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+    for (int i = 0; i < C::SL; ++i) {
+        const int dim = 16 * i + 4 * (mrow & 3);
+        const int slot = (dim >> 3) ^ vsw;
+        const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
+        st.o[i] = mfma16x16x16<DT>(phi, bv, st.o[i]);
+        st.o[i] = mfma16x16x16<DT>(plo, bv, st.o[i]);
     }
 }
 
@@ -292,23 +337,23 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     }
 }
 
-// Wave states -> LDS -> the split's partial for the heads in write_mask.
-// Every lane stores its unreduced state (P x V rows of its lane group, the
-// partial sum of its MFMA lane group) and, after one barrier, each thread
-// merges one float4 of the output over lane groups and waves by the
-// max-rescale rule.  (All waves of a block share one running maximum, so lane
-// groups add plainly; waves are rescaled to the workgroup maximum.)
+// Wave states -> LDS -> the split's partial for the heads in write_mask.  The
+// P x V rows are already per head; the sums of the four MFMA lane groups and
+// the waves are merged by the max-rescale rule, one float4 of output per
+// thread.
 template <int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
                              uint32_t write_mask) {
     using C = MCfg<D, GMAX, WAVES>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rg = lane / C::LPR, ch = lane % C::LPR;
     const int mrow = lane & 15, mq = lane >> 4;
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-        sm.fin.acc[wave][rg][g][2 * ch] = make_float4(st.o[g][0], st.o[g][1], st.o[g][2], st.o[g][3]);
-        sm.fin.acc[wave][rg][g][2 * ch + 1] = make_float4(st.o[g][4], st.o[g][5], st.o[g][6], st.o[g][7]);
+    for (int r = 0; r < 4; ++r) {
+        const int head = 4 * mq + r;
+        if (head < GMAX) {
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) sm.fin.acc[wave][head][16 * i + mrow] = st.o[i][r];
+        }
     }
     if (mrow < GMAX) {
         sm.fin.l[wave][mq][mrow] = st.l;
@@ -327,18 +372,8 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float f = rescale(sm.fin.m[w][g], mm);
-            float lw = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) lw += sm.fin.l[w][q][g];
-            float4 aw = sm.fin.acc[w][0][g][d4];
-#pragma unroll
-            for (int r = 1; r < C::RPI; ++r) {
-                const float4 x = sm.fin.acc[w][r][g][d4];
-                aw.x += x.x;
-                aw.y += x.y;
-                aw.z += x.z;
-                aw.w += x.w;
-            }
+            const float lw = (sm.fin.l[w][0][g] + sm.fin.l[w][1][g]) + (sm.fin.l[w][2][g] + sm.fin.l[w][3][g]);
+            const float4 aw = *reinterpret_cast<const float4 *>(&sm.fin.acc[w][g][4 * d4]);
             L = fmaf(lw, f, L);
             A.x = fmaf(aw.x, f, A.x);
             A.y = fmaf(aw.y, f, A.y);
@@ -473,7 +508,8 @@ hipError_t by_group(const PartialParams &p, hipStream_t s) {
     if (p.G <= 1) return by_paged<DT, D, 1>(p, s);
     if (p.G <= 2) return by_paged<DT, D, 2>(p, s);
     if (p.G <= 4) return by_paged<DT, D, 4>(p, s);
-    return by_paged<DT, D, 8>(p, s);
+    if (p.G <= 8) return by_paged<DT, D, 8>(p, s);
+    return by_paged<DT, D, 16>(p, s);
 }
 
 template <int DT>
@@ -486,8 +522,9 @@ hipError_t by_dim(const PartialParams &p, hipStream_t s) {
 bool mfma_supports(const PartialParams &p) {
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (p.d != 64 && p.d != 128) return false;
-    if (p.G > 8) return false;                          // register budget of the P x V accumulators
     if (p.page_size && p.page_size % kBlk) return false;   // a 16-token block must sit in one page
+    // unified-max weights reach e^64; fp16 operands would overflow past 65504
+    if (p.dtype == F16 && p.unified) return false;
     return true;
 }
 
