@@ -108,16 +108,18 @@ struct MCfg {
 template <int D, int GMAX, int WAVES>
 struct MSmem {
     using C = MCfg<D, GMAX, WAVES>;
-    struct {
-        uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tile
-        uint4 v[WAVES][kBlk * C::ROWB / 16];      // wave-private V tile
-        float corr[WAVES][16];                    // running-max rescale factors per head row
-    } loop;
-    struct {
-        float acc[WAVES][GMAX][D];                // each wave's P x V rows of the real heads
+    static constexpr int GQ = (GMAX + 3) / 4;      // head quads
+    struct Fin {
+        float4 acc[WAVES][D][GQ];                 // each wave's P x V rows: [dim][head quad]
         float l[WAVES][4][GMAX];                  // every MFMA lane group's partial sums
         float m[WAVES][GMAX];
-    } fin;
+    };
+    union {
+        uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tiles ...
+        Fin fin;                                  // ... reused by the epilogue once every wave is done
+    };
+    uint4 v[WAVES][kBlk * C::ROWB / 16];          // wave-private V tiles
+    float corr[WAVES][16];                        // running-max rescale factors per head row
     uint32_t bad[WAVES];
 };
 
@@ -210,8 +212,8 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = lane / C::LPR, ch = lane % C::LPR;
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
-    char *ktile = reinterpret_cast<char *>(sm.loop.k[wave]);
-    char *vtile = reinterpret_cast<char *>(sm.loop.v[wave]);
+    char *ktile = reinterpret_cast<char *>(sm.k[wave]);
+    char *vtile = reinterpret_cast<char *>(sm.v[wave]);
 #pragma unroll
     for (int i = 0; i < C::LI; ++i) {
         // K chunks arrive pre-swizzled (the load picked chunk ch ^ (row & (LPR-1)));
@@ -261,8 +263,8 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
         }
         // rescale the P x V accumulators (heads on rows 4 * (l / 16) + r)
         if (__any(moved)) {
-            if (lane < 16) sm.loop.corr[wave][lane] = corr;
-            const float4 cf = *reinterpret_cast<const float4 *>(&sm.loop.corr[wave][4 * mq]);
+            if (lane < 16) sm.corr[wave][lane] = corr;
+            const float4 cf = *reinterpret_cast<const float4 *>(&sm.corr[wave][4 * mq]);
 #pragma unroll
             for (int i = 0; i < C::SL; ++i) {
                 st.o[i][0] *= cf.x;
@@ -338,61 +340,77 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 }
 
 // Wave states -> LDS -> the split's partial for the heads in write_mask.  The
-// P x V rows are already per head; the sums of the four MFMA lane groups and
-// the waves are merged by the max-rescale rule, one float4 of output per
-// thread.
+// P x V rows are already per head (lane group q holds heads 4q .. 4q + 3 of
+// one dim per slice, one 16-byte LDS store each); after one barrier each
+// thread merges one dim of four heads over the waves by the max-rescale rule.
 template <int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
                              uint32_t write_mask) {
     using C = MCfg<D, GMAX, WAVES>;
+    constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mrow = lane & 15, mq = lane >> 4;
+    __syncthreads();   // the epilogue area overlays the K tiles of every wave
+    if (mq < GQ) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int head = 4 * mq + r;
-        if (head < GMAX) {
-#pragma unroll
-            for (int i = 0; i < C::SL; ++i) sm.fin.acc[wave][head][16 * i + mrow] = st.o[i][r];
-        }
+        for (int i = 0; i < C::SL; ++i)
+            sm.fin.acc[wave][16 * i + mrow][mq] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
     }
     if (mrow < GMAX) {
         sm.fin.l[wave][mq][mrow] = st.l;
         if (mq == 0) sm.fin.m[wave][mrow] = st.m;
     }
     __syncthreads();
-    constexpr int D4 = D / 4;
-    for (int idx = threadIdx.x; idx < p.G * D4; idx += C::THREADS) {
-        const int g = idx / D4, d4 = idx % D4;
-        if (!((write_mask >> g) & 1u)) continue;
-        float mm = sm.fin.m[0][g];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) mm = fmaxf(mm, sm.fin.m[w][g]);
-        float L = 0.f;
+    for (int idx = threadIdx.x; idx < GQ * D; idx += C::THREADS) {
+        const int gq = idx / D, dim = idx % D;
         float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+        float L[4] = {0.f, 0.f, 0.f, 0.f}, M[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * gq + r;
+            M[r] = -INFINITY;
+            if (g < GMAX) {
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) M[r] = fmaxf(M[r], sm.fin.m[w][g]);
+            }
+        }
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float f = rescale(sm.fin.m[w][g], mm);
-            const float lw = (sm.fin.l[w][0][g] + sm.fin.l[w][1][g]) + (sm.fin.l[w][2][g] + sm.fin.l[w][3][g]);
-            const float4 aw = *reinterpret_cast<const float4 *>(&sm.fin.acc[w][g][4 * d4]);
-            L = fmaf(lw, f, L);
-            A.x = fmaf(aw.x, f, A.x);
-            A.y = fmaf(aw.y, f, A.y);
-            A.z = fmaf(aw.z, f, A.z);
-            A.w = fmaf(aw.w, f, A.w);
+            const float4 aw = sm.fin.acc[w][dim][gq];
+            float f[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int g = 4 * gq + r;
+                f[r] = 0.f;
+                if (g < GMAX) {
+                    f[r] = rescale(sm.fin.m[w][g], M[r]);
+                    const float lw = (sm.fin.l[w][0][g] + sm.fin.l[w][1][g]) + (sm.fin.l[w][2][g] + sm.fin.l[w][3][g]);
+                    L[r] = fmaf(lw, f[r], L[r]);
+                }
+            }
+            A.x = fmaf(aw.x, f[0], A.x);
+            A.y = fmaf(aw.y, f[1], A.y);
+            A.z = fmaf(aw.z, f[2], A.z);
+            A.w = fmaf(aw.w, f[3], A.w);
         }
-        const size_t slot = slot0 + (size_t)g * p.max_splits;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<float4 *>(p.part_o + slot * D + 4 * d4) = make_float4(A.x * inv, A.y * inv, A.z * inv,
-                                                                               A.w * inv);
-        if (d4 == 0) {
-            p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
-            p.part_l[slot] = L;
+        const float a4[4] = {A.x, A.y, A.z, A.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * gq + r;
+            if (g >= p.G || !((write_mask >> g) & 1u)) continue;
+            const size_t slot = slot0 + (size_t)g * p.max_splits;
+            p.part_o[slot * D + dim] = L[r] > 0.f ? a4[r] / L[r] : 0.f;
+            if (dim == 0) {
+                p.part_m[slot] = (L[r] > 0.f && M[r] != -INFINITY) ? M[r] * kLn2 : -INFINITY;
+                p.part_l[slot] = L[r];
+            }
         }
     }
 }
 
-template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
-__global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialParams p) {
+template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNI>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4)))
+partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
@@ -430,7 +448,7 @@ __global__ void __launch_bounds__(64 * WAVES) partial_mfma_kernel(const PartialP
     const uint32_t all = (1u << G) - 1u;
     MState<D, GMAX> st;
     uint32_t badmask = 0;
-    if (p.unified) {
+    if constexpr (UNI) {
         st.init(p.phi2);
         scan_split<DT, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
         const uint64_t bal = __ballot(st.bad);
@@ -476,7 +494,12 @@ Shape launch_shape(const PartialParams &p) {
 template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
 hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
     dim3 grid(p.max_splits, p.Hkv, p.B);
-    hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED>), grid, dim3(64 * WAVES), 0, stream, p);
+    if (p.unified)
+        hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED, true>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED, false>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
