@@ -132,6 +132,18 @@ __device__ __forceinline__ void store_out(void *out, size_t idx, float val, int 
         reinterpret_cast<uint16_t *>(out)[idx] = float_to_f16_bits(val);
 }
 
+// Split handled by the workgroup at grid column x of (request b, KV head kvh).
+// Consecutive workgroups are dealt to the eight XCDs in turn, so with the split
+// index fastest in the grid, XCD i would get splits i, i + 8, ... of every
+// (request, KV head).  Requests shorter than the longest leave their high
+// splits empty, and the leftover splits beyond a multiple of eight would then
+// always land on the low XCDs (about 20% more work on XCD 0 than on XCD 7 for
+// lengths spread over 1k..16k).  Rotating the split index by the (request, KV
+// head) number deals those leftovers to the XCDs in turn.
+__device__ __forceinline__ int split_index(int x, int b, int kvh, int Hkv, int S) {
+    return (int)(((unsigned)x + (unsigned)(b * Hkv + kvh)) % (unsigned)S);
+}
+
 // Number of tokens of request b that the kernels read.
 __device__ __forceinline__ int request_len(const int32_t *seq_lens, int b, int cap, int limit) {
     int n = seq_lens ? seq_lens[b] : cap;

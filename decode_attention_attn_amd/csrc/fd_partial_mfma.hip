@@ -414,7 +414,8 @@ partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
     const int G = p.G, h0 = kvh * G;
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
     const int t0 = s * p.split;

@@ -223,7 +223,8 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     constexpr int E = C::E;
     __shared__ Smem<D, GMAX> sm;
 
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
     const int G = p.G, h0 = kvh * G;
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
     const int t0 = s * p.split;
