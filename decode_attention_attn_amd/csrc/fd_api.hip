@@ -41,6 +41,19 @@ fd_status validate_desc(const fd_decode_desc *d) {
     return FD_OK;
 }
 
+// Compute units of the current device, read once per device.
+int32_t device_cus() {
+    static int32_t cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 fd::PartialParams base_params(const fd_decode_desc *d) {
     fd::PartialParams p;
     memset(&p, 0, sizeof p);
@@ -59,6 +72,7 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     p.lo2 = (float)((double)d->lo * log2e);
     p.hi2 = (float)((double)d->hi * log2e);
     p.dtype = d->kv_dtype;
+    p.num_cus = device_cus();
     return p;
 }
 

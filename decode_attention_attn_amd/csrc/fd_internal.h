@@ -41,6 +41,7 @@ struct PartialParams {
     float phi2, lo2, hi2;       // unified max, log2 units
     int32_t unified;            // 1 = unified max with fallback
     int32_t dtype;              // DType of q, k, v
+    int32_t num_cus;            // compute units of the device (launch-shape choice only)
 };
 
 struct CombineParams {

@@ -164,11 +164,17 @@ __device__ __forceinline__ PageCache load_pages(const PartialParams &p, int b, i
 }
 
 template <int D, bool PAGED>
-__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, const PageCache &pc, int b, int kvh, int tb) {
+__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, const PageCache &pc, int b, int kvh, int tb,
+                                                int t1) {
     BlockRows r;
     r.tb = tb;
     r.page_ok = true;
     const size_t head_off = (size_t)kvh * D;
+    if (tb >= t1) {                                       // past the split: every row reads the safe row
+        r.page_ok = false;
+        r.row0 = head_off;
+        return r;
+    }
     if constexpr (PAGED) {
         const int pg = tb / p.page_size;                  // wave-uniform
         const int phys = pg - pc.base < 64 ? __builtin_amdgcn_readlane(pc.entry, pg - pc.base)
@@ -311,27 +317,26 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
     if constexpr (PF) {
         // ping-pong: block A computes while block B loads, then the roles swap
-        // (unrolled by two so no register copy has to wait on in-flight loads)
+        // (unrolled by two so no register copy has to wait on in-flight loads).
+        // Every step issues its loads unconditionally -- a block past the split
+        // reads the safe row -- so that each wait covers exactly one block's
+        // loads; a load under a branch would make the wait at the join cover
+        // the prefetch too.
         if (wave >= nblk) return;
-        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + wave * kBlk), rb = ra;
+        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + wave * kBlk, t1), rb = ra;
         uint4 ka[C::LI], va[C::LI], kb2[C::LI], vb2[C::LI];
         load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
         for (int blk = wave; blk < nblk; blk += 2 * WAVES) {
-            const bool has_b = blk + WAVES < nblk;
-            if (has_b) {
-                rb = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + WAVES) * kBlk);
-                load_block<D, GMAX, WAVES>(p, rb, t1, safe_row, kb2, vb2);
-            }
+            rb = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + WAVES) * kBlk, t1);
+            load_block<D, GMAX, WAVES>(p, rb, t1, safe_row, kb2, vb2);
             compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
-            if (blk + 2 * WAVES < nblk) {
-                ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + 2 * WAVES) * kBlk);
-                load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
-            }
-            if (has_b) compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + 2 * WAVES) * kBlk, t1);
+            load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
+            if (blk + WAVES < nblk) compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
         }
     } else {
         for (int blk = wave; blk < nblk; blk += WAVES) {
-            const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk);
+            const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
             uint4 kr[C::LI], vr[C::LI];
             load_block<D, GMAX, WAVES>(p, br, t1, safe_row, kr, vr);
             compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
@@ -478,18 +483,21 @@ partial_mfma_kernel(const PartialParams p) {
 }
 
 // Launch shape: waves per workgroup and whether a wave prefetches its next
-// block.  Chosen per group size from measurements on MI355X.
+// block.  Chosen from measurements on MI355X.
 struct Shape {
     int waves;
     bool prefetch;
 };
 
 Shape launch_shape(const PartialParams &p) {
-    // long-context GQA (G = 4, 1024 workgroups): 2 waves without prefetch
-    // measured 25.4 us against 27.5 (4 waves) and 29.1 (1 wave); groups of 8
-    // (160 VGPRs): 1 wave, 390 us against 433 us (2 waves) on B=4, N=128k
+    // groups of more than four heads: one wave per workgroup (B=4, N=128k,
+    // G=8 and B=64 paged batches measured no slower than with two)
     if (p.G > 4) return Shape{1, false};
-    return Shape{2, false};
+    // fewer than four workgroups per CU: each SIMD runs one or two waves and a
+    // wave's own load-then-compute chain sets the pace, so overlap the two
+    // (Llama-2-7B-shaped MHA, 512 workgroups: 14.7 us against 15.5 us)
+    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
+    return Shape{2, wgs < 4 * (int64_t)p.num_cus};
 }
 
 template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>

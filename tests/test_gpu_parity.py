@@ -185,6 +185,37 @@ def test_awkward_lengths(kernel, page):
     ft.check_partials(res, inp, 256, what=f"lengths page={page}")
 
 
+# both launch regimes of the MFMA kernel: a grid of fewer than four
+# workgroups per CU takes the prefetching two-wave shape, a larger one the
+# plain shape (groups above four heads: one wave); workgroups = splits of the
+# longest request x KV heads x requests, split 256
+REGIMES = [
+    (16, 16, (4096, 3000)),                   # G=1, 512 workgroups
+    (16, 16, (4096,) * 6 + (3001, 17)),       # G=1, 2048
+    (32, 8, (4096, 2900, 1)),                 # G=4, 384
+    (32, 8, (4096,) * 7 + (100,)),            # G=4, 1024
+    (64, 8, (4096,) * 8 + (2500,)),           # G=8, 1152
+]
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("mode", ["sync", "unified"])
+@pytest.mark.parametrize("Hq,Hkv,lens", REGIMES)
+def test_launch_regimes(Hq, Hkv, lens, mode, page):
+    base = synth.Workload("regime", B=1, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", split=256, N=1, page_size=page,
+                          stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, lens))
+    what = f"G={Hq // Hkv} B={len(lens)} {mode} page={page}"
+    say(f"[regime] {what}")
+    if mode == "sync":
+        res = Run(inp).run(kernel="mfma")
+        ft.check_partials(res, inp, 256, what=what)
+    else:
+        res = Run(inp).run(kernel="mfma", mode="unified", phi=-12.0, lo=-12.0, hi=12.0)
+        assert res["count"] == int(res["flags"].sum()) and 0 < res["count"] < res["flags"].size
+    ft.check_exact(res, inp, what=what)
+
+
 @pytest.mark.parametrize("page", [0, 16])
 def test_empty_request_gives_zero_and_minus_inf(page):
     base = synth.Workload("empty", B=3, Hq=8, Hkv=2, d=128, dtype="bf16", split=64, N=1, page_size=page)
