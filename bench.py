@@ -251,14 +251,22 @@ def cpu_baseline(inp, alg, seconds):
                       f"{el:.1f} s of fp64 oracle work, scaled to one step"}
 
 
-def traffic_from_profile(workload, kernel_name):
+def run_settings(args):
+    """The bench options that select which kernel runs and how."""
+    s = {"kernel": args.kernel, "mode": args.mode}
+    if args.mode == "unified":
+        s.update(phi=args.phi, lo=args.lo, hi=args.hi)
+    return s
+
+
+def traffic_from_profile(workload, kernel_name, settings):
     """HBM bytes per launch of the partial kernel from the committed PMC summary,
-    if its kernel-source hash matches the current sources; else None."""
+    if it was taken with the same kernel sources and run settings; else None."""
     f = ROOT / "profiles" / f"{workload}_pmc.json"
     if not f.exists():
         return None
     d = json.loads(f.read_text())
-    if d.get("source_hash") != source_hash():
+    if d.get("source_hash") != source_hash() or d.get("settings") != settings:
         return None
     k = d.get("kernels", {}).get(kernel_name)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -290,7 +298,7 @@ def main():
         summarize_profile(args.summarize_profile)
         return 0
     if args.pmc_summary:
-        pmc_summary(args.workload, *args.pmc_summary)
+        pmc_summary(args.workload, *args.pmc_summary, settings=run_settings(args))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
@@ -309,7 +317,7 @@ def main():
     log(f"[bench] step {g['step_ms'] * 1e3:.2f} us, partial {np.mean(g['part_us']):.2f} us, "
         f"combine {np.mean(g['comb_us']):.2f} us (back-to-back averages); parity {parity}")
     kname = "fd_decode_attn_paged" if w.page_size else PARTIAL_KERNEL
-    traffic = traffic_from_profile(w.name, kname)
+    traffic = traffic_from_profile(w.name, kname, run_settings(args))
     achieved = alg["partial"] / part_s / 1e9
     line = {
         "metric": "decode-attn us/step and achieved HBM TB/s (% of MI355X peak), N=32k GQA",
@@ -409,10 +417,11 @@ def _counter_means(d, counter):
     return {k: (len(v), float(np.mean(v))) for k, v in agg.items()}
 
 
-def pmc_summary(workload, fetch_dir, write_dir):
+def pmc_summary(workload, fetch_dir, write_dir, settings):
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the calibration copy of
-    COPY_BYTES.  Writes profiles/<workload>_pmc.json and prints a table."""
+    COPY_BYTES.  Writes profiles/<workload>_pmc.json and prints a table.
+    settings: the run options the counter runs used (pass the same ones)."""
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
     copy_name = "calibration copy" if "calibration copy" in fetch else None
@@ -420,7 +429,7 @@ def pmc_summary(workload, fetch_dir, write_dir):
         raise SystemExit("no calibration copy kernel in the FETCH_SIZE run (use --copy-calibration)")
     f_scale = COPY_BYTES / (fetch[copy_name][1] * 1024)
     w_scale = COPY_BYTES / (write[copy_name][1] * 1024)
-    out = {"workload": workload, "source_hash": source_hash(), "copy_bytes": COPY_BYTES,
+    out = {"workload": workload, "source_hash": source_hash(), "settings": settings, "copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     print(f"| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (scaled) |")
     print("|---|---|---|---|---|")
