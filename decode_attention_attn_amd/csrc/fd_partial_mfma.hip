@@ -187,25 +187,56 @@ __device__ __forceinline__ BlockRows block_rows(const PartialParams &p, const Pa
     return r;
 }
 
-// K (chunks XOR-swizzled by row) and V (natural) of a block, 16 bytes per lane each.
+// Block loads go through buffer resources: the wave-uniform base is the
+// block's first row, each lane's byte offset within a block is the same for
+// every block (computed once), and rows past the block's valid range lie
+// beyond num_records, so the hardware returns zeros for them without a memory
+// access.  Word 3 of a raw buffer resource on this GPU family: 32-bit data
+// format, no swizzle, no stride.
+constexpr int32_t kBufferWord3 = 0x00020000;
+constexpr int kLoadNT = 2;                            // cache policy: non-temporal (streamed once)
+
+template <int LI>
+struct LaneOffsets {
+    uint32_t k[LI], v[LI];
+};
+
 template <int D, int GMAX, int WAVES>
-__device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1, size_t safe_row,
-                                           uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
-                                           uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI]) {
+__device__ __forceinline__ LaneOffsets<MCfg<D, GMAX, WAVES>::LI> lane_offsets(const PartialParams &p) {
     using C = MCfg<D, GMAX, WAVES>;
     const int lane = threadIdx.x & 63;
     const int rg = lane / C::LPR, ch = lane % C::LPR;
-    const char *kb = static_cast<const char *>(p.k);
-    const char *vb = static_cast<const char *>(p.v);
-    const size_t rstride = (size_t)p.Hkv * D;
+    const uint32_t rbytes = (uint32_t)p.Hkv * D * 2;     // bytes between consecutive tokens of a head
+    LaneOffsets<C::LI> o;
 #pragma unroll
     for (int i = 0; i < C::LI; ++i) {
         const int r = i * C::RPI + rg;
-        const bool ok = br.page_ok && br.tb + r < t1;
-        const size_t row = ok ? br.row0 + r * rstride : safe_row;
-        const int kch = ch ^ (r & (C::LPR - 1));
-        kr[i] = load16_stream(kb + (row + kch * 8) * 2);
-        vr[i] = load16_stream(vb + (row + ch * 8) * 2);
+        o.k[i] = r * rbytes + 16 * (ch ^ (r & (C::LPR - 1)));   // K chunks XOR-swizzled by row
+        o.v[i] = r * rbytes + 16 * ch;                           // V natural
+    }
+    return o;
+}
+
+// K and V of a block, 16 bytes per lane each.
+template <int D, int GMAX, int WAVES>
+__device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1,
+                                           const LaneOffsets<MCfg<D, GMAX, WAVES>::LI> &off,
+                                           uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
+                                           uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI]) {
+    using C = MCfg<D, GMAX, WAVES>;
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const int valid = br.page_ok ? max(0, min(kBlk, t1 - br.tb)) : 0;   // wave-uniform
+    const int32_t bytes = valid * p.Hkv * D * 2;
+    const char *kb = static_cast<const char *>(p.k) + br.row0 * 2;
+    const char *vb = static_cast<const char *>(p.v) + br.row0 * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), 0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, bytes, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < C::LI; ++i) {
+        const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[i], 0, kLoadNT);
+        const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rv, off.v[i], 0, kLoadNT);
+        kr[i] = make_uint4(a.x, a.y, a.z, a.w);
+        vr[i] = make_uint4(c.x, c.y, c.z, c.w);
     }
 }
 
@@ -310,35 +341,45 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
                            MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const size_t head_off = (size_t)kvh * D;
-    // a row every lane may read in place of an absent one (its weight is 0)
-    const size_t safe_row = PAGED ? head_off : (((size_t)b * p.kv_capacity + t0) * p.Hkv) * D + head_off;
+    const auto off = lane_offsets<D, GMAX, WAVES>(p);
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
     const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
     if constexpr (PF) {
         // ping-pong: block A computes while block B loads, then the roles swap
         // (unrolled by two so no register copy has to wait on in-flight loads).
-        // Every step issues its loads unconditionally -- a block past the split
-        // reads the safe row -- so that each wait covers exactly one block's
-        // loads; a load under a branch would make the wait at the join cover
-        // the prefetch too.
-        if (wave >= nblk) return;
-        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + wave * kBlk, t1), rb = ra;
+        // The loop runs while a full A-B-A step remains and issues its loads
+        // unconditionally; the last one or two blocks are peeled off.  A load
+        // under a branch would make the compiler's wait at the join cover the
+        // prefetched block as well, and a load past the split would make the
+        // epilogue wait for a useless block.
+        const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
+        if (n == 0) return;
+        const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
+        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1), rb;
         uint4 ka[C::LI], va[C::LI], kb2[C::LI], vb2[C::LI];
-        load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
-        for (int blk = wave; blk < nblk; blk += 2 * WAVES) {
-            rb = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + WAVES) * kBlk, t1);
-            load_block<D, GMAX, WAVES>(p, rb, t1, safe_row, kb2, vb2);
+        load_block<D, GMAX, WAVES>(p, ra, t1, off, ka, va);
+        int j = 0;
+        for (; j + 2 < n; j += 2) {
+            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+            load_block<D, GMAX, WAVES>(p, rb, t1, off, kb2, vb2);
             compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
-            ra = block_rows<D, PAGED>(p, pc, b, kvh, t0 + (blk + 2 * WAVES) * kBlk, t1);
-            load_block<D, GMAX, WAVES>(p, ra, t1, safe_row, ka, va);
-            if (blk + WAVES < nblk) compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            ra = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 2) * tstep, t1);
+            load_block<D, GMAX, WAVES>(p, ra, t1, off, ka, va);
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+        }
+        if (j + 2 == n) {
+            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+            load_block<D, GMAX, WAVES>(p, rb, t1, off, kb2, vb2);
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+        } else {
+            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
         }
     } else {
         for (int blk = wave; blk < nblk; blk += WAVES) {
             const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
             uint4 kr[C::LI], vr[C::LI];
-            load_block<D, GMAX, WAVES>(p, br, t1, safe_row, kr, vr);
+            load_block<D, GMAX, WAVES>(p, br, t1, off, kr, vr);
             compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
         }
     }
