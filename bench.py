@@ -208,6 +208,18 @@ def run_gpu(args, inp, wl):
                 res=res, S=S, device=torch.cuda.get_device_name(0))
 
 
+def fallback_stats(inp, flags, args):
+    """Flagged (request, query head, split) triples of the last step, out of those
+    that hold tokens; each flagged one was recomputed with the synchronized softmax."""
+    w = inp.w
+    S = flags.shape[-1]
+    per_req = np.minimum(-(-inp.seq_lens.astype(np.int64) // w.split), S)
+    valid = int(per_req.sum()) * w.Hq
+    n = int(flags.astype(np.int64).sum())
+    return {"flagged_splits": n, "splits_with_tokens": valid, "rate": n / max(valid, 1),
+            "phi": args.phi, "lo": args.lo, "hi": args.hi}
+
+
 def parity_spot_check(inp, res, rows):
     import oracle
     p = oracle.problem_of(inp)
@@ -347,6 +359,8 @@ def main():
         "parity": parity,
         "device": g["device"],
     }
+    if args.mode == "unified":
+        line["fallback"] = fallback_stats(inp, g["res"]["flags"], args)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(inp, alg, args.cpu_seconds)
