@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
 CPU-baseline leg import this module.  It shares no code with the GPU library
 (decode_attention_attn_amd) and neither imports the other.  Arguments are
 numpy arrays in the storage conventions of the `synth` module (f32 -> float32,
-f16 -> float16, bf16 -> uint16 bit patterns); results are float64.
+f16 -> float16, bf16 -> uint16 bit patterns, fp8 (OCP E4M3, K and V only) ->
+uint8 bit patterns); results are float64.
 
 The arithmetic and its citations are in oracle.c; this file only marshals.
 """
@@ -23,15 +24,16 @@ LIB = _HERE / "liboracle.so"
 BUILD_CMD = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              str(SRC), "-o", str(LIB), "-lm"]
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 _NAME = {v: k for k, v in DTYPE_CODE.items()}
-_NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+_NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 class OracleProblem(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("dtype", C.c_int32), ("N", C.c_int32), ("page_size", C.c_int32),
-                ("max_blocks", C.c_int32), ("scale", C.c_double)]
+                ("max_blocks", C.c_int32), ("scale", C.c_double), ("q_dtype", C.c_int32),
+                ("k_scale", C.c_double), ("v_scale", C.c_double)]
 
 
 def build() -> Path:
@@ -100,17 +102,23 @@ def _i32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
 
 
-def problem(B, Hq, Hkv, d, dtype, N=0, page_size=0, max_blocks=0, scale=None):
+def problem(B, Hq, Hkv, d, dtype, N=0, page_size=0, max_blocks=0, scale=None, q_dtype=None, k_scale=1.0,
+            v_scale=1.0):
+    """dtype: storage of K and V; q_dtype: storage of q (default: dtype; bf16 for fp8 caches)."""
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    return OracleProblem(B, Hq, Hkv, d, DTYPE_CODE[dtype], N, page_size, max_blocks, float(scale))
+    if q_dtype is None:
+        q_dtype = "bf16" if dtype == "fp8" else dtype
+    return OracleProblem(B, Hq, Hkv, d, DTYPE_CODE[dtype], N, page_size, max_blocks, float(scale),
+                         DTYPE_CODE[q_dtype], float(k_scale), float(v_scale))
 
 
 def problem_of(inp, scale=None):
     """OracleProblem for a synth.Inputs bundle."""
     w = inp.w
     return problem(w.B, w.Hq, w.Hkv, w.d, w.dtype, N=w.N, page_size=w.page_size,
-                   max_blocks=w.max_blocks if w.page_size else 0, scale=scale)
+                   max_blocks=w.max_blocks if w.page_size else 0, scale=scale, q_dtype=w.q_dtype,
+                   k_scale=w.k_scale, v_scale=w.v_scale)
 
 
 def _rows_arg(rows):
@@ -124,7 +132,7 @@ def attention(p, q, k, v, seq_lens=None, block_table=None, rows=None, threads=No
     """Exact attention.  Returns (out [B*Hq, d], lse [B*Hq]) as float64; rows not
     selected are NaN."""
     dtype = _NAME[p.dtype]
-    q, k, v = _storage(q, dtype), _storage(k, dtype), _storage(v, dtype)
+    q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
     out = np.full((p.B * p.Hq, p.d), np.nan)
@@ -139,7 +147,7 @@ def attention(p, q, k, v, seq_lens=None, block_table=None, rows=None, threads=No
 def split_partials(p, q, k, v, split, S_max, seq_lens=None, block_table=None, rows=None, threads=None):
     """Per-split (O_s normalised, m_s, l_s): shapes [B*Hq, S_max, d], [B*Hq, S_max] x2."""
     dtype = _NAME[p.dtype]
-    q, k, v = _storage(q, dtype), _storage(k, dtype), _storage(v, dtype)
+    q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
     R = p.B * p.Hq
@@ -193,7 +201,7 @@ def unified_max(p, q, k, v, split, S_max, phi, lo, hi, seq_lens=None, block_tabl
     """Unified-max softmax with per-split fallback.  Returns a dict with out, lse,
     part_o/part_m/part_l, flags [B*Hq, S_max] (uint8) and n_flagged."""
     dtype = _NAME[p.dtype]
-    q, k, v = _storage(q, dtype), _storage(k, dtype), _storage(v, dtype)
+    q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
     R = p.B * p.Hq

@@ -32,6 +32,13 @@
  *        "Asynchronized Softmax with Unified Max Value" (Eq. 3, Eq. 4,
  *        "The Overflow Fallback: Recomputation", Figure 6).
  *
+ *   8-bit KV cache: the handbook page lists KV caches stored in FP8 and read
+ *   in wide loads, converted in registers (section "A paged decode attention
+ *   kernel (with GQA)", its list of improvements; section on the KV cache's
+ *   size names KV cache quantization).  The format is OCP FP8 E4M3 (OCP 8-bit
+ *   Floating Point Specification, "E4M3"); a stored K or V value means
+ *   stored * k_scale or stored * v_scale (one scale per tensor).
+ *
  * Readings taken where the pages leave a step open:
  *   - the last split holds the remainder n - (S-1)*split tokens;
  *   - a split with no tokens is reported as m = -inf, l = 0, O = 0;
@@ -58,14 +65,18 @@
 #define ODT_F32 0
 #define ODT_F16 1
 #define ODT_BF16 2
+#define ODT_FP8_E4M3 3   /* K and V only */
 
 typedef struct {
     int32_t B, Hq, Hkv, d;
-    int32_t dtype;       /* ODT_* : storage type of q, k and v                */
+    int32_t dtype;       /* ODT_* : storage type of k and v                   */
     int32_t N;           /* contiguous: token capacity per request            */
     int32_t page_size;   /* 0 -> contiguous [B][N][Hkv][d]; else paged        */
     int32_t max_blocks;  /* paged: row length of block_table                  */
     double scale;        /* score = scale * <q, k>                            */
+    int32_t q_dtype;     /* ODT_F32 / F16 / BF16: storage type of q           */
+    double k_scale;      /* a stored K value means stored * k_scale            */
+    double v_scale;      /* a stored V value means stored * v_scale            */
 } oracle_problem;
 
 /* ---------------------------------------------------------------------- */
@@ -92,11 +103,28 @@ static double bf16_bits_to_double(uint16_t b)
     return (double)f;
 }
 
+/* OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+ * is subnormal (m * 2^-9); S.1111.111 is NaN; there are no infinities, the
+ * largest finite magnitude is 448. */
+static double e4m3_bits_to_double(uint8_t b)
+{
+    int sign = b >> 7, e = (b >> 3) & 0xf, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);                  /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp((double)(m | 8), e - 10);        /* 1.m * 2^(e-7)         */
+    return sign ? -v : v;
+}
+
 static double elem(const void *base, int dtype, size_t i)
 {
     switch (dtype) {
     case ODT_F32: return (double)((const float *)base)[i];
     case ODT_F16: return f16_bits_to_double(((const uint16_t *)base)[i]);
+    case ODT_FP8_E4M3: return e4m3_bits_to_double(((const uint8_t *)base)[i]);
     default:      return bf16_bits_to_double(((const uint16_t *)base)[i]);
     }
 }
@@ -127,7 +155,10 @@ static int check_problem(const oracle_problem *p, const int32_t *seq_lens, const
 {
     if (!p || p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0) return ORACLE_EINVAL;
     if (p->Hq % p->Hkv) return ORACLE_EINVAL;
-    if (p->dtype < ODT_F32 || p->dtype > ODT_BF16) return ORACLE_EINVAL;
+    if (p->dtype < ODT_F32 || p->dtype > ODT_FP8_E4M3) return ORACLE_EINVAL;
+    if (p->q_dtype < ODT_F32 || p->q_dtype > ODT_BF16) return ORACLE_EINVAL;
+    if (!(p->k_scale > 0.0) || !(p->v_scale > 0.0) || isinf(p->k_scale) || isinf(p->v_scale))
+        return ORACLE_EINVAL;
     if (p->page_size < 0) return ORACLE_EINVAL;
     if (p->page_size > 0 && (!block_table || p->max_blocks <= 0)) return ORACLE_EINVAL;
     for (int b = 0; b < p->B; ++b) {
@@ -149,7 +180,7 @@ static void scores(const oracle_problem *p, const void *q, const void *k, const 
         size_t koff = kv_row(p, block_table, b, t, kvh);
         double dot = 0.0;
         for (int i = 0; i < p->d; ++i)
-            dot += elem(q, p->dtype, qoff + i) * elem(k, p->dtype, koff + i);
+            dot += elem(q, p->q_dtype, qoff + i) * (p->k_scale * elem(k, p->dtype, koff + i));
         s[t - t0] = dot * p->scale;
     }
 }
@@ -170,7 +201,7 @@ static double weighted_v(const oracle_problem *p, const void *v, const int32_t *
     for (int i = 0; i < p->d; ++i) o[i] = 0.0;
     for (int t = t0; t < t1; ++t) {
         size_t voff = kv_row(p, block_table, b, t, kvh);
-        for (int i = 0; i < p->d; ++i) o[i] += s[t - t0] * elem(v, p->dtype, voff + i);
+        for (int i = 0; i < p->d; ++i) o[i] += s[t - t0] * (p->v_scale * elem(v, p->dtype, voff + i));
     }
     for (int i = 0; i < p->d; ++i) o[i] = den > 0.0 ? o[i] / den : 0.0;
     return den;

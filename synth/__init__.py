@@ -18,6 +18,10 @@ Storage conventions (what the arrays hold):
   f32  -> numpy float32
   f16  -> numpy float16
   bf16 -> numpy uint16 holding the bfloat16 bit pattern
+  fp8  -> numpy uint8 holding an OCP FP8 E4M3 bit pattern (K and V only; q
+          is bf16).  A cache tensor with scale c stores x / c rounded to
+          nearest even and saturated at +-448, for the N(0, 1) draw x; the
+          value it stands for is stored * c.
 """
 from __future__ import annotations
 
@@ -28,9 +32,11 @@ import numpy as np
 
 SEED_Q, SEED_K, SEED_V, SEED_PERM, SEED_LENS, SEED_STRESS = 1, 2, 3, 7, 11, 13
 
-DTYPES = ("f32", "f16", "bf16")
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = ("f32", "f16", "bf16", "fp8")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+E4M3_MAX = 448.0
+E4M3_QNAN = 0x7F
 BF16_QNAN = 0x7FC0
 F16_QNAN = 0x7E00
 
@@ -55,6 +61,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP FP8 E4M3 bits, nearest even, saturated at +-448 (torch's encoder)."""
+    import torch
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of E4M3 bits to fp32 (torch's decoder)."""
+    import torch
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    return torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
     """fp32 values -> storage array of `dtype` (rounded to nearest even)."""
     if dtype == "f32":
@@ -63,26 +83,33 @@ def encode(x: np.ndarray, dtype: str) -> np.ndarray:
         return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if dtype == "fp8":
+        return f32_to_e4m3_bits(x)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def decode_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage array -> exact float64 values (for building expected shapes in tests)."""
+    """Storage array -> exact float64 values (for building expected shapes in tests).
+    For fp8 this is the stored value, before the tensor's scale."""
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_bits_to_f32(a).astype(np.float64)
     return np.asarray(a).astype(np.float64)
 
 
 def nan_value(dtype: str):
-    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(BF16_QNAN)}[dtype]
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(BF16_QNAN),
+            "fp8": np.uint8(E4M3_QNAN)}[dtype]
 
 
-_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 _CHUNK = 1 << 20
 
 
-def normal(seed: int, shape, dtype: str) -> np.ndarray:
-    """Standard normal draws from PCG64(seed), rounded to `dtype` storage.
+def normal(seed: int, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Standard normal draws from PCG64(seed), rounded to `dtype` storage
+    (fp8: the draw divided by `scale`, see the module docstring).
 
     Drawn in chunks through reused buffers (one pass over the output, no
     full-size temporaries); the values are the generator's sequence in order.
@@ -106,6 +133,8 @@ def normal(seed: int, shape, dtype: str) -> np.ndarray:
             np.add(tm, um, out=tm)
             np.right_shift(tm, 16, out=tm)
             flat[i:i + m] = tm
+        elif dtype == "fp8":
+            flat[i:i + m] = f32_to_e4m3_bits(buf[:m] / np.float32(scale))
         else:
             flat[i:i + m] = buf[:m]
     return out
@@ -130,6 +159,15 @@ class Workload:
     stress_frac: float = 0.0    # Bernoulli fraction of key rows (b, t, kvh) scaled by stress_scale
     stress_scale: float = 8.0
     fixed_lens: Optional[tuple] = None  # explicit per-request lengths (overrides len_range)
+    qdtype: Optional[str] = None        # storage of q; None -> dtype (bf16 for an fp8 cache)
+    k_scale: float = 1.0                # fp8 caches: a stored K value stands for stored * k_scale
+    v_scale: float = 1.0
+
+    @property
+    def q_dtype(self) -> str:
+        if self.qdtype is not None:
+            return self.qdtype
+        return "bf16" if self.dtype == "fp8" else self.dtype
 
     @property
     def G(self) -> int:
@@ -152,6 +190,9 @@ WORKLOADS = {
                                   N=16384, len_range=(1024, 16384), page_size=16),
     "umax_stress": Workload("umax_stress", B=4, Hq=64, Hkv=8, d=128, dtype="bf16", split=256, N=131072,
                             stress_frac=0.02, stress_scale=8.0),
+    # the long-context GQA shape with an 8-bit cache (scale 1/64: N(0, 1) draws stored as 64 x)
+    "long_gqa_32k_fp8": Workload("long_gqa_32k_fp8", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256,
+                                 N=32768, k_scale=1.0 / 64, v_scale=1.0 / 64),
 }
 
 
@@ -210,15 +251,15 @@ def make_inputs(w: Workload, poison_tail: bool = True) -> Inputs:
     set to NaN, so that a kernel that reads or weights them shows it.
     """
     lens = seq_lens_for(w)
-    q = normal(SEED_Q, (w.B, w.Hq, w.d), w.dtype)
+    q = normal(SEED_Q, (w.B, w.Hq, w.d), w.q_dtype)
     table = None
     if w.page_size:
         table, P = block_table_for(w, lens)
         shape = (P, w.page_size, w.Hkv, w.d)
     else:
         shape = (w.B, w.N, w.Hkv, w.d)
-    k = normal(SEED_K, shape, w.dtype)
-    v = normal(SEED_V, shape, w.dtype)
+    k = normal(SEED_K, shape, w.dtype, w.k_scale)
+    v = normal(SEED_V, shape, w.dtype, w.v_scale)
 
     mask = None
     if w.stress_frac > 0:

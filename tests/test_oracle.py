@@ -90,6 +90,68 @@ def test_decode_bf16_all_patterns_match_fp32_widening():
     np.testing.assert_array_equal(got, want)
 
 
+def test_decode_e4m3_all_patterns_match_torch_and_the_ocp_table():
+    """8-bit cache values: OCP FP8 E4M3 (the handbook page's list of kernel
+    improvements names FP8 KV caches converted in registers)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(codes, "fp8")
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    # the specification's landmarks: max normal S.1111.110 = 448, min normal
+    # S.0001.000 = 2^-6, max subnormal S.0000.111 = 0.875 * 2^-6, min subnormal
+    # S.0000.001 = 2^-9, one = S.0111.000
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x07] == 0.875 * 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0x38] == 1.0 and got[0x00] == 0.0 and got[0x80] == 0.0 and math.copysign(1, got[0x80]) < 0
+
+
+def _fp8_problem(rng, B, Hq, Hkv, d, N, k_scale, v_scale):
+    q = synth.encode(rng.standard_normal((B, Hq, d)).astype(np.float32), "bf16")
+    k = synth.encode(rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 40, "fp8")
+    v = synth.encode(rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 40, "fp8")
+    p = oracle.problem(B, Hq, Hkv, d, "fp8", N=N, q_dtype="bf16", k_scale=k_scale, v_scale=v_scale)
+    return p, q, k, v
+
+
+def test_brute_force_fp8_cache_with_scales():
+    """A stored K or V value stands for stored * scale (one scale per tensor)."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, d, N = 1, 4, 2, 8, 7
+    ks, vs = 0.037, 1.9
+    p, q, k, v = _fp8_problem(rng, B, Hq, Hkv, d, N, ks, vs)
+    out, lse = oracle.attention(p, q, k, v)
+    dq = synth.decode_f64(q, "bf16")
+    dk = synth.decode_f64(k, "fp8") * ks
+    dv = synth.decode_f64(v, "fp8") * vs
+    bo, bl = brute_force(dq, dk, dv, None)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_fp8_cache_equals_the_fp32_cache_of_its_values_bitwise():
+    """With power-of-two scales the dequantised values are exact fp32 numbers:
+    the fp8 problem and the fp32 problem over those numbers agree bit for bit."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, d, N = 2, 8, 2, 16, 40
+    p8, q, k, v = _fp8_problem(rng, B, Hq, Hkv, d, N, 2.0 ** -6, 2.0 ** 3)
+    lens = np.array([40, 13], np.int32)
+    o8, l8 = oracle.attention(p8, q, k, v, seq_lens=lens)
+    q32 = synth.decode_f64(q, "bf16").astype(np.float32)
+    k32 = (synth.decode_f64(k, "fp8") * 2.0 ** -6).astype(np.float32)
+    v32 = (synth.decode_f64(v, "fp8") * 2.0 ** 3).astype(np.float32)
+    p32 = oracle.problem(B, Hq, Hkv, d, "f32", N=N)
+    o32, l32 = oracle.attention(p32, q32, k32, v32, seq_lens=lens)
+    assert np.array_equal(o8, o32) and np.array_equal(l8, l32)
+    # the same for the split partials
+    a = oracle.split_partials(p8, q, k, v, 16, 3, seq_lens=lens)
+    b = oracle.split_partials(p32, q32, k32, v32, 16, 3, seq_lens=lens)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 # ----------------------------------------------------------------------------
 # the handbook's worked online-softmax exercise
 # ----------------------------------------------------------------------------
