@@ -69,9 +69,10 @@ def algorithmic_bytes(inp):
     import synth
     w = inp.w
     eb = synth.ELEM_BYTES[w.dtype]
+    qb = synth.ELEM_BYTES[w.q_dtype]       # q and out (out has q's type)
     kv = inp.kv_bytes
-    q = w.B * w.Hq * w.d * eb
-    out = w.B * w.Hq * w.d * eb
+    q = w.B * w.Hq * w.d * qb
+    out = w.B * w.Hq * w.d * qb
     table = 0
     if w.page_size:
         table = int(((inp.seq_lens.astype(np.int64) + w.page_size - 1) // w.page_size).sum()) * 4
@@ -94,14 +95,14 @@ def run_gpu(args, inp, wl):
         torch.cuda.synchronize()
         del src, dst
 
-    def dev_t(a):
+    def dev_t(a, dtype):
         a = np.ascontiguousarray(a)
-        if w.dtype == "bf16":
+        if dtype == "bf16":
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    q = dev_t(inp.q)
-    k0, v0 = dev_t(inp.k), dev_t(inp.v)
+    q = dev_t(inp.q, w.q_dtype)
+    k0, v0 = dev_t(inp.k, w.dtype), dev_t(inp.v, w.dtype)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
     table = torch.from_numpy(inp.block_table).to(dev) if w.page_size else None
     kv_bytes = k0.numel() * k0.element_size() * 2
@@ -113,8 +114,9 @@ def run_gpu(args, inp, wl):
     log(f"[bench] {w.name}: {copies} KV copies of {kv_bytes / 2**20:.1f} MiB")
 
     mode = args.mode
+    f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
     desc = fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, split_size=w.split, max_seq_len=w.N, mode=mode,
-                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel)
+                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel, **f8)
     S = desc.max_splits
     out = torch.empty((w.B, w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device=dev)
     lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)

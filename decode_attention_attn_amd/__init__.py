@@ -18,11 +18,11 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = _PKG / "libfd_decode_attn.so"
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_HIP = range(5)
-FD_F32, FD_F16, FD_BF16 = 0, 1, 2
+FD_F32, FD_F16, FD_BF16, FD_FP8_E4M3 = 0, 1, 2, 3
 FD_SOFTMAX_SYNC, FD_SOFTMAX_UNIFIED_MAX = 0, 1
 FD_KERNEL_AUTO, FD_KERNEL_VALU, FD_KERNEL_MFMA = 0, 1, 2
 
-DTYPES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16}
+DTYPES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8": FD_FP8_E4M3}
 MODES = {"sync": FD_SOFTMAX_SYNC, "unified": FD_SOFTMAX_UNIFIED_MAX}
 KERNELS = {"auto": FD_KERNEL_AUTO, "valu": FD_KERNEL_VALU, "mfma": FD_KERNEL_MFMA}
 
@@ -37,20 +37,26 @@ class fd_decode_desc(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("kv_dtype", C.c_int32), ("out_dtype", C.c_int32), ("split_size", C.c_int32),
                 ("max_splits", C.c_int32), ("scale", C.c_float), ("mode", C.c_int32),
-                ("phi", C.c_float), ("lo", C.c_float), ("hi", C.c_float), ("kernel", C.c_int32)]
+                ("phi", C.c_float), ("lo", C.c_float), ("hi", C.c_float), ("kernel", C.c_int32),
+                ("q_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 def make_desc(B, Hq, Hkv, d, kv_dtype="bf16", out_dtype=None, split_size=256, max_splits=None,
-              max_seq_len=None, scale=0.0, mode="sync", phi=0.0, lo=0.0, hi=0.0, kernel="auto"):
+              max_seq_len=None, scale=0.0, mode="sync", phi=0.0, lo=0.0, hi=0.0, kernel="auto", q_dtype=None,
+              k_scale=0.0, v_scale=0.0):
     """Descriptor with names instead of enum codes.  max_splits defaults to
-    ceil(max_seq_len / split_size)."""
+    ceil(max_seq_len / split_size); q_dtype (8-bit caches only) defaults to
+    bf16, and out_dtype to the type of q."""
     if max_splits is None:
         if max_seq_len is None:
             raise ValueError("give max_splits or max_seq_len")
         max_splits = max(1, -(-int(max_seq_len) // int(split_size)))
+    if q_dtype is None:
+        q_dtype = "bf16" if kv_dtype == "fp8" else kv_dtype
     return fd_decode_desc(int(B), int(Hq), int(Hkv), int(d), DTYPES[kv_dtype],
-                          DTYPES[out_dtype or kv_dtype], int(split_size), int(max_splits), float(scale),
-                          MODES[mode], float(phi), float(lo), float(hi), KERNELS[kernel])
+                          DTYPES[out_dtype or q_dtype], int(split_size), int(max_splits), float(scale),
+                          MODES[mode], float(phi), float(lo), float(hi), KERNELS[kernel], DTYPES[q_dtype],
+                          float(k_scale), float(v_scale))
 
 
 _lib = None
@@ -109,8 +115,14 @@ def _torch():
 
 
 def _tdtype(code):
+    """torch dtype(s) a tensor of this storage type may have (8-bit: E4M3 or raw bytes)."""
     torch = _torch()
-    return {FD_F32: torch.float32, FD_F16: torch.float16, FD_BF16: torch.bfloat16}[code]
+    return {FD_F32: torch.float32, FD_F16: torch.float16, FD_BF16: torch.bfloat16,
+            FD_FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}[code]
+
+
+def _qdtype(desc):
+    return _tdtype(desc.q_dtype if desc.kv_dtype == FD_FP8_E4M3 else desc.kv_dtype)
 
 
 def _ptr(t, name, dtype=None, numel=None, optional=False):
@@ -125,7 +137,7 @@ def _ptr(t, name, dtype=None, numel=None, optional=False):
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
@@ -159,7 +171,7 @@ def fd_decode_attn_partial(desc, q, k, v, kv_capacity, seq_lens, part_o, part_m,
     kvt = _tdtype(desc.kv_dtype)
     nrow = desc.B * desc.Hq * desc.max_splits
     args = [
-        _ptr(q, "q", kvt, desc.B * desc.Hq * desc.d),
+        _ptr(q, "q", _qdtype(desc), desc.B * desc.Hq * desc.d),
         _ptr(k, "k", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         _ptr(v, "v", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         C.c_int32(int(kv_capacity)),
@@ -206,7 +218,7 @@ def fd_decode_attn_paged(desc, q, k_cache, v_cache, page_size, block_table, seq_
     if workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError(f"workspace needs {ws_bytes} bytes")
     args = [
-        _ptr(q, "q", kvt, desc.B * desc.Hq * desc.d),
+        _ptr(q, "q", _qdtype(desc), desc.B * desc.Hq * desc.d),
         _ptr(k_cache, "k_cache", kvt),
         _ptr(v_cache, "v_cache", kvt),
         C.c_int32(num_pages), C.c_int32(int(page_size)),

@@ -23,7 +23,11 @@ fd_status validate_desc(const fd_decode_desc *d) {
     if (d->Hq % d->Hkv) return FD_ERR_INVALID_ARG;
     if (d->Hq / d->Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
     if (d->d != 64 && d->d != 128) return FD_ERR_UNSUPPORTED;
-    if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_BF16) return FD_ERR_INVALID_ARG;
+    if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
+    if (d->kv_dtype == FD_FP8_E4M3) {
+        if (d->q_dtype != FD_F16 && d->q_dtype != FD_BF16) return FD_ERR_INVALID_ARG;
+        if (!finite(d->k_scale) || !finite(d->v_scale)) return FD_ERR_INVALID_ARG;
+    }
     if (d->out_dtype < FD_F32 || d->out_dtype > FD_BF16) return FD_ERR_INVALID_ARG;
     if (d->split_size < 1 || d->split_size > kMaxSplitSize) return FD_ERR_INVALID_ARG;
     if (d->max_splits < 1 || d->max_splits > kMaxSplits) return FD_ERR_INVALID_ARG;
@@ -64,7 +68,14 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     p.d = d->d;
     p.split = d->split_size;
     p.max_splits = d->max_splits;
-    const double scale = d->scale > 0.f ? (double)d->scale : (double)(1.0f / sqrtf((float)d->d));
+    double scale = d->scale > 0.f ? (double)d->scale : (double)(1.0f / sqrtf((float)d->d));
+    p.q_dtype = d->kv_dtype;
+    p.v_mult = 1.f;
+    if (d->kv_dtype == FD_FP8_E4M3) {   // stored K / V values stand for stored * scale
+        p.q_dtype = d->q_dtype;
+        scale *= d->k_scale > 0.f ? (double)d->k_scale : 1.0;
+        p.v_mult = d->v_scale > 0.f ? d->v_scale : 1.f;
+    }
     const double log2e = 1.4426950408889634;
     p.scale_log2 = (float)(scale * log2e);
     p.unified = d->mode == FD_SOFTMAX_UNIFIED_MAX;

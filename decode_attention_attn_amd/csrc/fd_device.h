@@ -16,6 +16,9 @@ template <int DT> struct Storage;
 template <> struct Storage<F32> { static constexpr int E = 4; static constexpr int bytes = 4; };
 template <> struct Storage<F16> { static constexpr int E = 8; static constexpr int bytes = 2; };
 template <> struct Storage<BF16> { static constexpr int E = 8; static constexpr int bytes = 2; };
+// 8-bit caches are read 8 bytes per lane so that a lane holds as many elements
+// as with a 16-bit cache
+template <> struct Storage<FP8> { static constexpr int E = 8; static constexpr int bytes = 1; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -27,11 +30,25 @@ __device__ __forceinline__ float f16_bits_to_float(uint32_t h16) {
     return (float)h;
 }
 
-// Widen the 16 bytes in `raw` to E fp32 values.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Widen the E elements in `raw` (16 bytes; 8 for FP8) to fp32.  The E4M3
+// conversion of gfx950 (v_cvt_pk_f32_fp8) is exact for all 256 codes,
+// NaN included.
 template <int DT>
 __device__ __forceinline__ void unpack(const uint4 &raw, float *out) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    if constexpr (DT == F32) {
+    if constexpr (DT == FP8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            out[4 * i] = a.x;
+            out[4 * i + 1] = a.y;
+            out[4 * i + 2] = b.x;
+            out[4 * i + 3] = b.y;
+        }
+    } else if constexpr (DT == F32) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
     } else if constexpr (DT == BF16) {
@@ -57,6 +74,19 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One lane's piece of a cache row: E elements (16 bytes; 8 for FP8), streamed.
+template <int DT>
+__device__ __forceinline__ uint4 load_piece(const void *p) {
+    if constexpr (Storage<DT>::E * Storage<DT>::bytes == 16) {
+        return load16_stream(p);
+    } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        return make_uint4(v.x, v.y, 0u, 0u);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // cross-lane reductions inside aligned lane groups of W (W | 64)

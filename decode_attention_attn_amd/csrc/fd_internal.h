@@ -16,7 +16,7 @@ constexpr int kMaxSplitSize = 1 << 20;
 // fp32 headroom for sums of up to 2^20 terms times |v|
 constexpr float kMaxUnifiedRange = 64.f;
 
-enum DType : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
+enum DType : int32_t { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };   // FP8: OCP E4M3, K and V only
 
 // Everything a split-partial kernel reads.  Scores are handled in log2
 // units: s2 = scale * log2(e) * <q, k>, so that exp(s - m) = exp2(s2 - m2).
@@ -40,7 +40,9 @@ struct PartialParams {
     float scale_log2;           // scale * log2(e)
     float phi2, lo2, hi2;       // unified max, log2 units
     int32_t unified;            // 1 = unified max with fallback
-    int32_t dtype;              // DType of q, k, v
+    int32_t dtype;              // DType of k and v (and of q unless FP8)
+    int32_t q_dtype;            // DType of q (F16 or BF16 when dtype is FP8)
+    float v_mult;               // FP8: value of one stored V unit (v_scale); else 1
     int32_t num_cus;            // compute units of the device (launch-shape choice only)
 };
 

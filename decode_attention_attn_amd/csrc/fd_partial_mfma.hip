@@ -94,6 +94,23 @@ __device__ __forceinline__ void split_probs(const float (&pr)[4], s16x4 &hi, s16
 
 constexpr int kBlk = 16;   // tokens per MFMA block
 
+// Instantiation type T: the 16-bit operand type of the matrix instructions
+// (F16 or BF16, also the type of q), plus 16 when the cache holds 8-bit E4M3
+// values that are widened to it in registers (exactly: an E4M3 value has four
+// significant bits and its exponent range fits both 16-bit types).
+constexpr int kF8 = 16;
+__host__ __device__ constexpr int op_of(int T) { return T & 15; }
+__host__ __device__ constexpr bool f8_of(int T) { return T >= kF8; }
+
+// How a block's cache rows are loaded: 16 bytes per lane, LPR lanes per row.
+template <int T, int D>
+struct KLoad {
+    static constexpr int EB = f8_of(T) ? 1 : 2;     // bytes per cache element
+    static constexpr int LPR = D * EB / 16;         // lanes per row
+    static constexpr int RPI = 64 / LPR;            // rows per load instruction
+    static constexpr int LI = kBlk / RPI;           // load instructions per block (K, and again V)
+};
+
 template <int D, int GMAX, int WAVES>
 struct MCfg {
     static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension (QK)
@@ -201,34 +218,35 @@ struct LaneOffsets {
     uint32_t k[LI], v[LI];
 };
 
-template <int D, int GMAX, int WAVES>
-__device__ __forceinline__ LaneOffsets<MCfg<D, GMAX, WAVES>::LI> lane_offsets(const PartialParams &p) {
-    using C = MCfg<D, GMAX, WAVES>;
+template <int T, int D>
+__device__ __forceinline__ LaneOffsets<KLoad<T, D>::LI> lane_offsets(const PartialParams &p) {
+    using L = KLoad<T, D>;
     const int lane = threadIdx.x & 63;
-    const int rg = lane / C::LPR, ch = lane % C::LPR;
-    const uint32_t rbytes = (uint32_t)p.Hkv * D * 2;     // bytes between consecutive tokens of a head
-    LaneOffsets<C::LI> o;
+    const int rg = lane / L::LPR, ch = lane % L::LPR;
+    const uint32_t rbytes = (uint32_t)p.Hkv * D * L::EB;   // bytes between consecutive tokens of a head
+    LaneOffsets<L::LI> o;
 #pragma unroll
-    for (int i = 0; i < C::LI; ++i) {
-        const int r = i * C::RPI + rg;
-        o.k[i] = r * rbytes + 16 * (ch ^ (r & (C::LPR - 1)));   // K chunks XOR-swizzled by row
-        o.v[i] = r * rbytes + 16 * ch;                           // V natural
+    for (int i = 0; i < L::LI; ++i) {
+        const int r = i * L::RPI + rg;
+        // 16-bit K chunks arrive XOR-swizzled by row; 8-bit rows are swizzled
+        // when widened into the tile
+        o.k[i] = r * rbytes + 16 * (f8_of(T) ? ch : (ch ^ (r & (L::LPR - 1))));
+        o.v[i] = r * rbytes + 16 * ch;
     }
     return o;
 }
 
 // K and V of a block, 16 bytes per lane each.
-template <int D, int GMAX, int WAVES>
+template <int T, int D>
 __device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1,
-                                           const LaneOffsets<MCfg<D, GMAX, WAVES>::LI> &off,
-                                           uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
-                                           uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI]) {
-    using C = MCfg<D, GMAX, WAVES>;
+                                           const LaneOffsets<KLoad<T, D>::LI> &off,
+                                           uint4 (&kr)[KLoad<T, D>::LI], uint4 (&vr)[KLoad<T, D>::LI]) {
+    using C = KLoad<T, D>;
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     const int valid = br.page_ok ? max(0, min(kBlk, t1 - br.tb)) : 0;   // wave-uniform
-    const int32_t bytes = valid * p.Hkv * D * 2;
-    const char *kb = static_cast<const char *>(p.k) + br.row0 * 2;
-    const char *vb = static_cast<const char *>(p.v) + br.row0 * 2;
+    const int32_t bytes = valid * p.Hkv * D * C::EB;
+    const char *kb = static_cast<const char *>(p.k) + br.row0 * C::EB;
+    const char *vb = static_cast<const char *>(p.v) + br.row0 * C::EB;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), 0, bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, bytes, kBufferWord3);
 #pragma unroll
@@ -240,24 +258,58 @@ __device__ __forceinline__ void load_block(const PartialParams &p, const BlockRo
     }
 }
 
-template <int DT, int D, int GMAX, int WAVES, bool UNIFIED>
+// 16 E4M3 values -> 16 values of the operand type, as two 16-byte chunks.
+template <int OP>
+__device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
+        if constexpr (OP == BF16) {   // exact: the top 16 bits hold every E4M3 value
+            o[2 * i] = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+            o[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
+        } else {                      // exact: every E4M3 value is an f16 value
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+        }
+    }
+    lo = make_uint4(o[0], o[1], o[2], o[3]);
+    hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
 __device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int t1,
-                                              const uint4 (&kr)[MCfg<D, GMAX, WAVES>::LI],
-                                              const uint4 (&vr)[MCfg<D, GMAX, WAVES>::LI], const uint4 (&qop)[D / 32],
+                                              const uint4 (&kr)[KLoad<T, D>::LI],
+                                              const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
                                               MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
+    using L = KLoad<T, D>;
+    constexpr int DT = op_of(T);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rg = lane / C::LPR, ch = lane % C::LPR;
+    const int rg = lane / L::LPR, ch = lane % L::LPR;
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
     char *ktile = reinterpret_cast<char *>(sm.k[wave]);
     char *vtile = reinterpret_cast<char *>(sm.v[wave]);
+    // tiles: 16-byte chunk c of row r lives at slot c ^ (r & (LPR-1)) (K) and
+    // c ^ (2 * (r & (LPR/2 - 1))) (V), LPR = D / 8 chunks per row
 #pragma unroll
-    for (int i = 0; i < C::LI; ++i) {
-        // K chunks arrive pre-swizzled (the load picked chunk ch ^ (row & (LPR-1)));
-        // V chunk ch of row r goes to slot ch ^ (2 * (r & (LPR/2 - 1)))
-        const int r = i * C::RPI + rg;
-        *reinterpret_cast<uint4 *>(ktile + i * C::RPI * C::ROWB + lane * 16) = kr[i];
-        *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
+    for (int i = 0; i < L::LI; ++i) {
+        const int r = i * L::RPI + rg;
+        if constexpr (f8_of(T)) {   // this lane's 16 values are chunks 2 ch and 2 ch + 1
+            uint4 k0, k1, v0, v1;
+            widen_f8<DT>(kr[i], k0, k1);
+            widen_f8<DT>(vr[i], v0, v1);
+            const int c = 2 * ch, ks = r & (C::LPR - 1), vs = 2 * (r & (C::LPR / 2 - 1));
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c ^ ks)) = k0;
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * ((c + 1) ^ ks)) = k1;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (c ^ vs)) = v0;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * ((c + 1) ^ vs)) = v1;
+        } else {                    // K chunks arrive pre-swizzled
+            *reinterpret_cast<uint4 *>(ktile + i * L::RPI * C::ROWB + lane * 16) = kr[i];
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
+        }
     }
 
     // ---- S^T = K q^T on the matrix cores
@@ -336,12 +388,12 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
 // computed, so a wave keeps two blocks in flight.  Paged caches read the
 // split's block-table entries once (one per lane) and pick each block's page
 // from them with a lane read.
-template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
 __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
                            MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
-    using C = MCfg<D, GMAX, WAVES>;
+    using L = KLoad<T, D>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const auto off = lane_offsets<D, GMAX, WAVES>(p);
+    const auto off = lane_offsets<T, D>(p);
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
     const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
     if constexpr (PF) {
@@ -356,31 +408,31 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
         if (n == 0) return;
         const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
         BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1), rb;
-        uint4 ka[C::LI], va[C::LI], kb2[C::LI], vb2[C::LI];
-        load_block<D, GMAX, WAVES>(p, ra, t1, off, ka, va);
+        uint4 ka[L::LI], va[L::LI], kb2[L::LI], vb2[L::LI];
+        load_block<T, D>(p, ra, t1, off, ka, va);
         int j = 0;
         for (; j + 2 < n; j += 2) {
             rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
-            load_block<D, GMAX, WAVES>(p, rb, t1, off, kb2, vb2);
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            load_block<T, D>(p, rb, t1, off, kb2, vb2);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
             ra = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 2) * tstep, t1);
-            load_block<D, GMAX, WAVES>(p, ra, t1, off, ka, va);
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            load_block<T, D>(p, ra, t1, off, ka, va);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
         }
         if (j + 2 == n) {
             rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
-            load_block<D, GMAX, WAVES>(p, rb, t1, off, kb2, vb2);
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            load_block<T, D>(p, rb, t1, off, kb2, vb2);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
         } else {
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
         }
     } else {
         for (int blk = wave; blk < nblk; blk += WAVES) {
             const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
-            uint4 kr[C::LI], vr[C::LI];
-            load_block<D, GMAX, WAVES>(p, br, t1, off, kr, vr);
-            compute_block<DT, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
+            uint4 kr[L::LI], vr[L::LI];
+            load_block<T, D>(p, br, t1, off, kr, vr);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
         }
     }
 }
@@ -389,7 +441,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 // P x V rows are already per head (lane group q holds heads 4q .. 4q + 3 of
 // one dim per slice, one 16-byte LDS store each); after one barrier each
 // thread merges one dim of four heads over the waves by the max-rescale rule.
-template <int D, int GMAX, int WAVES>
+template <int T, int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
                              uint32_t write_mask) {
     using C = MCfg<D, GMAX, WAVES>;
@@ -445,7 +497,9 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
             const int g = 4 * gq + r;
             if (g >= p.G || !((write_mask >> g) & 1u)) continue;
             const size_t slot = slot0 + (size_t)g * p.max_splits;
-            p.part_o[slot * D + dim] = L[r] > 0.f ? a4[r] / L[r] : 0.f;
+            float o = L[r] > 0.f ? a4[r] / L[r] : 0.f;
+            if constexpr (f8_of(T)) o *= p.v_mult;   // a stored V unit stands for v_scale
+            p.part_o[slot * D + dim] = o;
             if (dim == 0) {
                 p.part_m[slot] = (L[r] > 0.f && M[r] != -INFINITY) ? M[r] * kLn2 : -INFINITY;
                 p.part_l[slot] = L[r];
@@ -454,7 +508,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     }
 }
 
-template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNI>
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4)))
 partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
@@ -497,7 +551,7 @@ partial_mfma_kernel(const PartialParams p) {
     uint32_t badmask = 0;
     if constexpr (UNI) {
         st.init(p.phi2);
-        scan_split<DT, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
         const uint64_t bal = __ballot(st.bad);
         const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
         if (lane == 0) sm.bad[wave] = mine;
@@ -505,19 +559,19 @@ partial_mfma_kernel(const PartialParams p) {
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
         badmask &= all;
-        finish_split<D, GMAX, WAVES>(p, st, sm, slot0, all & ~badmask);
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, all & ~badmask);
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<DT, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
-            finish_split<D, GMAX, WAVES>(p, st, sm, slot0, badmask);
+            scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+            finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, badmask);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<DT, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
-        finish_split<D, GMAX, WAVES>(p, st, sm, slot0, all);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, all);
     }
     if (p.flags && threadIdx.x < G)
         p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
@@ -541,67 +595,60 @@ Shape launch_shape(const PartialParams &p) {
     return Shape{2, wgs < 4 * (int64_t)p.num_cus};
 }
 
-template <int DT, int D, int GMAX, int WAVES, bool PF, bool PAGED>
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED>
 hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
     dim3 grid(p.max_splits, p.Hkv, p.B);
     if (p.unified)
-        hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED, true>), grid, dim3(64 * WAVES), 0,
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, true>), grid, dim3(64 * WAVES), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL((partial_mfma_kernel<DT, D, GMAX, WAVES, PF, PAGED, false>), grid, dim3(64 * WAVES), 0,
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, false>), grid, dim3(64 * WAVES), 0,
                            stream, p);
     return hipGetLastError();
 }
 
-template <int DT, int D, int GMAX, bool PAGED>
+template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
-    const Shape sh = launch_shape(p);
-    constexpr bool four_fit = sizeof(MSmem<D, GMAX, 4>) <= 65536;
-    switch (sh.waves * 2 + (sh.prefetch ? 1 : 0)) {
-    case 2: return launch_shaped<DT, D, GMAX, 1, false, PAGED>(p, stream);
-    case 3: return launch_shaped<DT, D, GMAX, 1, true, PAGED>(p, stream);
-    case 5: return launch_shaped<DT, D, GMAX, 2, true, PAGED>(p, stream);
-    case 8:
-        if constexpr (four_fit) return launch_shaped<DT, D, GMAX, 4, false, PAGED>(p, stream);
-        return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
-    case 9:
-        if constexpr (four_fit) return launch_shaped<DT, D, GMAX, 4, true, PAGED>(p, stream);
-        return launch_shaped<DT, D, GMAX, 2, true, PAGED>(p, stream);
-    default: return launch_shaped<DT, D, GMAX, 2, false, PAGED>(p, stream);
+    if constexpr (GMAX > 4) {
+        return launch_shaped<T, D, GMAX, 1, false, PAGED>(p, stream);
+    } else {
+        return launch_shape(p).prefetch ? launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream)
+                                        : launch_shaped<T, D, GMAX, 2, false, PAGED>(p, stream);
     }
 }
 
-template <int DT, int D, int GMAX>
+template <int T, int D, int GMAX>
 hipError_t by_paged(const PartialParams &p, hipStream_t s) {
-    return p.page_size ? launch<DT, D, GMAX, true>(p, s) : launch<DT, D, GMAX, false>(p, s);
+    return p.page_size ? launch<T, D, GMAX, true>(p, s) : launch<T, D, GMAX, false>(p, s);
 }
 
-template <int DT, int D>
+template <int T, int D>
 hipError_t by_group(const PartialParams &p, hipStream_t s) {
-    if (p.G <= 1) return by_paged<DT, D, 1>(p, s);
-    if (p.G <= 2) return by_paged<DT, D, 2>(p, s);
-    if (p.G <= 4) return by_paged<DT, D, 4>(p, s);
-    if (p.G <= 8) return by_paged<DT, D, 8>(p, s);
-    return by_paged<DT, D, 16>(p, s);
+    if (p.G <= 1) return by_paged<T, D, 1>(p, s);
+    if (p.G <= 2) return by_paged<T, D, 2>(p, s);
+    if (p.G <= 4) return by_paged<T, D, 4>(p, s);
+    if (p.G <= 8) return by_paged<T, D, 8>(p, s);
+    return by_paged<T, D, 16>(p, s);
 }
 
-template <int DT>
+template <int T>
 hipError_t by_dim(const PartialParams &p, hipStream_t s) {
-    return p.d == 64 ? by_group<DT, 64>(p, s) : by_group<DT, 128>(p, s);
+    return p.d == 64 ? by_group<T, 64>(p, s) : by_group<T, 128>(p, s);
 }
 
 }  // namespace
 
 bool mfma_supports(const PartialParams &p) {
-    if (p.dtype != F16 && p.dtype != BF16) return false;
+    if (p.dtype != F16 && p.dtype != BF16 && p.dtype != FP8) return false;
     if (p.d != 64 && p.d != 128) return false;
     if (p.page_size && p.page_size % kBlk) return false;   // a 16-token block must sit in one page
     // unified-max weights reach e^64; fp16 operands would overflow past 65504
-    if (p.dtype == F16 && p.unified) return false;
+    if (p.q_dtype == F16 && p.unified) return false;
     return true;
 }
 
 hipError_t launch_partial_mfma(const PartialParams &p, hipStream_t stream) {
+    if (p.dtype == FP8) return p.q_dtype == F16 ? by_dim<kF8 + F16>(p, stream) : by_dim<kF8 + BF16>(p, stream);
     return p.dtype == F16 ? by_dim<F16>(p, stream) : by_dim<BF16>(p, stream);
 }
 

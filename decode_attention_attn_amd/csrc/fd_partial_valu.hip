@@ -94,8 +94,8 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
             const int t = tb + (wave * R + r) * RPW + rg;
             ok[r] = t < t1;
             const size_t off = (row_offset<PAGED, D>(p, b, kvh, ok[r] ? t : t0, ok[r]) + (size_t)c * E) * C::BYTES;
-            kr[r] = ok[r] ? load16_stream(kb + off) : make_uint4(0, 0, 0, 0);
-            vr[r] = ok[r] ? load16_stream(vb + off) : make_uint4(0, 0, 0, 0);
+            kr[r] = ok[r] ? load_piece<DT>(kb + off) : make_uint4(0, 0, 0, 0);
+            vr[r] = ok[r] ? load_piece<DT>(vb + off) : make_uint4(0, 0, 0, 0);
         }
         float s[R][GMAX];
 #pragma unroll
@@ -209,7 +209,9 @@ __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Sme
             A += sm.acc[w][g][dim] * f;
         }
         const size_t slot = slot0 + (size_t)g * p.max_splits;
-        p.part_o[slot * D + dim] = L > 0.f ? A / L : 0.f;
+        float o = L > 0.f ? A / L : 0.f;
+        if constexpr (DT == FP8) o *= p.v_mult;
+        p.part_o[slot * D + dim] = o;
         if (dim == 0) {
             p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
             p.part_l[slot] = L;
@@ -248,8 +250,16 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
         if (g < G) {
-            const size_t off = (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * C::BYTES;
-            unpack<DT>(load16(qb + off), qv[g]);
+            if constexpr (DT == FP8) {   // q is f16 or bf16
+                const uint4 raw = load16(qb + (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * 2);
+                if (p.q_dtype == BF16)
+                    unpack<BF16>(raw, qv[g]);
+                else
+                    unpack<F16>(raw, qv[g]);
+            } else {
+                const size_t off = (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * C::BYTES;
+                unpack<DT>(load16(qb + off), qv[g]);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) qv[g][e] = 0.f;
@@ -321,6 +331,7 @@ hipError_t launch_partial_valu(const PartialParams &p, hipStream_t stream) {
     switch (p.dtype) {
     case F32: return by_dim<F32>(p, stream);
     case F16: return by_dim<F16>(p, stream);
+    case FP8: return by_dim<FP8>(p, stream);
     default: return by_dim<BF16>(p, stream);
     }
 }

@@ -21,7 +21,13 @@
  *    up at the caller's next synchronisation, not in the status.
  *  - Tensors are dense, row-major, with 16-byte aligned base pointers; offsets
  *    are computed in 64 bits.
- *  - q has shape [B, Hq, d] and the same element type as the cache.
+ *  - q has shape [B, Hq, d] and the same element type as the cache, except
+ *    with an 8-bit cache, where q is f16 or bf16 (desc->q_dtype).
+ *  - 8-bit caches (FD_FP8_E4M3, OCP FP8 E4M3: bias 7, no infinities, largest
+ *    finite 448, S.1111.111 = NaN) stand for stored * k_scale and
+ *    stored * v_scale (one scale per tensor); the handbook page lists caches
+ *    stored in FP8, read in wide loads and converted in registers (section
+ *    "A paged decode attention kernel (with GQA)", its list of improvements).
  *  - GQA: query head h reads KV head h / (Hq / Hkv); consecutive query heads
  *    share a KV head (page "FlashAttention and inference kernels", section
  *    "A paged decode attention kernel (with GQA)").  Hq must be a multiple
@@ -61,7 +67,7 @@ typedef enum fd_status {
     FD_ERR_HIP = 4                   /* the HIP runtime rejected a launch */
 } fd_status;
 
-typedef enum fd_dtype { FD_F32 = 0, FD_F16 = 1, FD_BF16 = 2 } fd_dtype;
+typedef enum fd_dtype { FD_F32 = 0, FD_F16 = 1, FD_BF16 = 2, FD_FP8_E4M3 = 3 /* K and V only */ } fd_dtype;
 
 /* Softmax scaling inside a split.
  * SYNC: each split tracks its own running maximum (the FlashAttention online
@@ -79,13 +85,14 @@ typedef enum fd_softmax_mode { FD_SOFTMAX_SYNC = 0, FD_SOFTMAX_UNIFIED_MAX = 1 }
 typedef enum fd_kernel {
     FD_KERNEL_AUTO = 0,  /* the fastest kernel for the shape */
     FD_KERNEL_VALU = 1,  /* vector-ALU dot products; every dtype */
-    FD_KERNEL_MFMA = 2   /* matrix-core q-group x K^T; f16 / bf16 only */
+    FD_KERNEL_MFMA = 2   /* matrix cores; 16- and 8-bit caches, d in {64, 128}, pages of a
+                            multiple of 16 tokens; not with f16 q in UNIFIED_MAX mode */
 } fd_kernel;
 
 typedef struct fd_decode_desc {
     int32_t B, Hq, Hkv, d;   /* batch, query heads, KV heads, head dimension */
-    int32_t kv_dtype;        /* fd_dtype of q, K and V */
-    int32_t out_dtype;       /* fd_dtype of out */
+    int32_t kv_dtype;        /* fd_dtype of K and V (and of q, unless FD_FP8_E4M3) */
+    int32_t out_dtype;       /* fd_dtype of out (not FD_FP8_E4M3) */
     int32_t split_size;      /* tokens per split, 1..2^20; a multiple of page_size when paged */
     int32_t max_splits;      /* S_max, the split extent of the partial buffers, 1..4096;
                                 max_splits * split_size < 2^31 */
@@ -96,6 +103,10 @@ typedef struct fd_decode_desc {
                                 |hi - phi| <= 64, so that exp(s - phi) of an in-range
                                 score and its sums stay finite, normal fp32 numbers. */
     int32_t kernel;          /* fd_kernel */
+    int32_t q_dtype;         /* FD_FP8_E4M3 caches: fd_dtype of q, FD_F16 or FD_BF16;
+                                ignored otherwise (q has kv_dtype) */
+    float k_scale, v_scale;  /* FD_FP8_E4M3 caches: a stored K / V value stands for
+                                stored * scale; <= 0 selects 1; ignored otherwise */
 } fd_decode_desc;
 
 /* Split-partial kernel over a contiguous cache.

@@ -4,6 +4,8 @@ through its C ABI, and compare with the fp64 oracle under the stated bar.
 Tolerances (elementwise |got - ref| <= atol + rtol * |ref|, reference in fp64):
   fp16 / bf16 cache with fp32 accumulation: atol 2e-3, rtol 1e-2
   fp32 cache: atol 1e-5, rtol 1e-5
+  8-bit (E4M3) cache: as 16-bit caches (the values are exact; q is bf16 and
+  the accumulation fp32)
 Block-table indexing is checked bit-exactly elsewhere (permutation tests).
 """
 from __future__ import annotations
@@ -16,7 +18,7 @@ import decode_attention_attn_amd as fd
 import oracle
 import synth
 
-TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "fp8": (2e-3, 1e-2)}
 # scores within this distance of a unified-max bound may round to either side
 FLAG_MARGIN = 1e-3
 
@@ -77,7 +79,7 @@ class Run:
         self.inp = inp
         w = inp.w
         self.w = w
-        self.q = to_dev(inp.q, w.dtype)
+        self.q = to_dev(inp.q, w.q_dtype)
         self.k = to_dev(inp.k, w.dtype)
         self.v = to_dev(inp.v, w.dtype)
         t = torch()
@@ -88,9 +90,10 @@ class Run:
              max_splits=None):
         w = self.w
         split = split or w.split
+        f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
         return fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, out_dtype, split_size=split,
                             max_splits=max_splits or max(1, -(-w.N // split)), mode=mode, phi=phi, lo=lo,
-                            hi=hi, kernel=kernel)
+                            hi=hi, kernel=kernel, **f8)
 
     def run(self, use_lens=True, **kw):
         """Partial + combine (contiguous) or the paged entry point.  Returns a dict

@@ -166,6 +166,26 @@ def test_partial_rejects_bad_enum_codes_and_negative_capacity():
     assert _partial_status(desc, kv_capacity=-1) == fd.FD_ERR_INVALID_ARG
 
 
+def test_fp8_descriptor_validation():
+    """8-bit caches need an f16 or bf16 q, finite scales and a 16/32-bit output."""
+    ok = fd.make_desc(1, 8, 8, 128, "fp8", max_splits=4, k_scale=0.5, v_scale=2.0)
+    assert ok.q_dtype == fd.FD_BF16 and ok.out_dtype == fd.FD_BF16
+    assert _partial_status(ok) == fd.FD_ERR_INVALID_ARG          # valid desc, NULL tensors
+    bad = fd.make_desc(1, 8, 8, 128, "fp8", max_splits=4, q_dtype="f32")
+    assert _partial_status(bad) == fd.FD_ERR_INVALID_ARG
+    bad = fd.make_desc(1, 8, 8, 128, "fp8", max_splits=4, k_scale=float("inf"))
+    assert _partial_status(bad) == fd.FD_ERR_INVALID_ARG
+    bad = fd.make_desc(1, 8, 8, 128, "fp8", max_splits=4, v_scale=float("nan"))
+    assert _partial_status(bad) == fd.FD_ERR_INVALID_ARG
+    bad = fd.make_desc(1, 8, 8, 128, "fp8", max_splits=4, out_dtype="fp8")
+    assert _partial_status(bad) == fd.FD_ERR_INVALID_ARG
+    # q_dtype is ignored for 16-bit caches
+    other = fd.make_desc(0, 8, 8, 128, "bf16", max_splits=4)
+    other.q_dtype = 99
+    assert _partial_status(other) == fd.FD_OK
+    assert fd.fd_workspace_bytes(ok) == fd.fd_workspace_bytes(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4))
+
+
 def test_empty_batch_is_a_no_op():
     desc = fd.make_desc(0, 8, 8, 128, "bf16", max_splits=4)
     assert _partial_status(desc) == fd.FD_OK

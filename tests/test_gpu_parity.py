@@ -8,6 +8,7 @@ cases cover the edges: ragged and empty requests, every dtype, head
 dimension and group size, split sizes from 1 token to a single split,
 poisoned cache tails, invalid page entries, and the unified-max fallback.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -429,3 +430,75 @@ def test_unified_max_no_flags_in_a_wide_range(kernel):
     ft.check_exact(res, inp, what="unified, nothing flagged")
     valid = res["part_l"] > 0
     assert np.all(np.abs(res["part_m"][valid] - (-30.0)) < 1e-5)
+
+
+# ----------------------------------------------------------------------------
+# 8-bit (OCP E4M3) caches with per-tensor scales
+# ----------------------------------------------------------------------------
+def _fp8_workload(name, B, Hq, Hkv, d, qdt, lens, page=0, split=256, ks=1.0 / 64, vs=1.0 / 64, **kw):
+    base = synth.Workload(name, B=B, Hq=Hq, Hkv=Hkv, d=d, dtype="fp8", split=split, N=1, page_size=page,
+                          qdtype=qdt, k_scale=ks, v_scale=vs, **kw)
+    return synth.make_inputs(synth.with_lens(base, lens))
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (16, 2)])
+def test_fp8_cache_shapes(kernel, qdt, d, Hq, Hkv):
+    inp = _fp8_workload("fp8", 3, Hq, Hkv, d, qdt, (1000, 1, 385), split=128, ks=0.037, vs=1.9)
+    res = Run(inp).run(kernel=kernel)
+    what = f"fp8 {kernel} q={qdt} d={d} G={Hq // Hkv}"
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 128, what=what)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("page", [0, 16])
+def test_fp8_cache_equals_the_bf16_cache_of_its_values_bitwise(kernel, page):
+    """Power-of-two scales make the dequantised values exact bf16 numbers, and
+    the widening is exact: both caches give the same bits."""
+    inp8 = _fp8_workload("fp8eq", 2, 32, 8, 128, "bf16", (3000, 517), page=page)
+    w16 = dataclasses.replace(inp8.w, dtype="bf16", qdtype=None, k_scale=1.0, v_scale=1.0)
+    k16 = synth.f32_to_bf16_bits((synth.decode_f64(inp8.k, "fp8") * inp8.w.k_scale).astype(np.float32))
+    v16 = synth.f32_to_bf16_bits((synth.decode_f64(inp8.v, "fp8") * inp8.w.v_scale).astype(np.float32))
+    inp16 = synth.Inputs(w16, inp8.q, k16, v16, inp8.seq_lens, inp8.block_table)
+    a = Run(inp8).run(kernel=kernel)
+    b = Run(inp16).run(kernel=kernel)
+    for key in ("out", "lse", "part_m", "part_l"):
+        assert np.array_equal(a[key], b[key]), key
+    valid = a["part_l"] > 0
+    assert np.array_equal(a["part_o"][valid], b["part_o"][valid])
+    ft.check_exact(a, inp8, what=f"fp8 {kernel} page={page}")
+
+
+def test_fp8_paged_batched_shape():
+    inp = _fp8_workload("fp8paged", 6, 64, 8, 128, "bf16", (16384, 1024, 7000, 16, 4097, 2500), page=16)
+    res = Run(inp).run()
+    rows = ft.sample_rows(inp.w, 96, seed=6)
+    ft.check_exact(res, inp, rows=rows, what="fp8 paged")
+    ft.check_partials(res, inp, 256, rows=rows, what="fp8 paged")
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+def test_fp8_unified_max_flags_and_fallback(qdt):
+    inp = _fp8_workload("fp8umax", 2, 32, 4, 128, qdt, (4096, 1500), stress_frac=0.02, stress_scale=8.0)
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = Run(inp).run(mode="unified", phi=phi, lo=lo, hi=hi)
+    must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may])
+    assert res["count"] == int(got.sum()) and 0 < got.sum() < got.size
+    ft.check_exact(res, inp, what=f"fp8 unified q={qdt}")
+
+
+def test_fp8_long_context_gqa_full():
+    w = synth.WORKLOADS["long_gqa_32k_fp8"]
+    say("[long_gqa_32k_fp8] generating")
+    inp = synth.make_inputs(w)
+    res = Run(inp).run()
+    e1, e2 = ft.check_exact(res, inp, what="long_gqa_32k_fp8")
+    ft.check_partials(res, inp, w.split, what="long_gqa_32k_fp8")
+    say(f"[long_gqa_32k_fp8] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
