@@ -259,20 +259,21 @@ __device__ __forceinline__ void load_block(const PartialParams &p, const BlockRo
 }
 
 // 16 E4M3 values -> 16 values of the operand type, as two 16-byte chunks.
+// gfx950's v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1 converts two values
+// per instruction, exactly for all 256 codes (checked on the hardware): an
+// E4M3 value has four significant bits and its exponents fit both types.
 template <int OP>
 __device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     uint32_t o[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
-        if constexpr (OP == BF16) {   // exact: the top 16 bits hold every E4M3 value
-            o[2 * i] = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
-            o[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
-        } else {                      // exact: every E4M3 value is an f16 value
-            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
-            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+        if constexpr (OP == BF16) {
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+        } else {
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
         }
     }
     lo = make_uint4(o[0], o[1], o[2], o[3]);
@@ -585,14 +586,19 @@ struct Shape {
 };
 
 Shape launch_shape(const PartialParams &p) {
+    // 8-bit caches: a block is half the bytes for the same compute, so a wave
+    // without prefetch waits out a memory round trip per 4 KiB; always overlap
+    const bool f8 = p.dtype == FP8;
     // groups of more than four heads: one wave per workgroup (B=4, N=128k,
     // G=8 and B=64 paged batches measured no slower than with two)
-    if (p.G > 4) return Shape{1, false};
+    if (p.G > 4) return Shape{1, f8};
     // fewer than four workgroups per CU: each SIMD runs one or two waves and a
     // wave's own load-then-compute chain sets the pace, so overlap the two
     // (Llama-2-7B-shaped MHA, 512 workgroups: 14.7 us against 15.5 us)
     const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
-    return Shape{2, wgs < 4 * (int64_t)p.num_cus};
+    // (8-bit, 32k GQA: 2 waves 15.6 us, 4 waves 18.5 us -- 152 VGPRs leave
+    // room for 12 waves per CU, not the 16 that four 4-wave workgroups need)
+    return Shape{2, f8 || wgs < 4 * (int64_t)p.num_cus};
 }
 
 template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED>
@@ -610,7 +616,10 @@ hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
 template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
     if constexpr (GMAX > 4) {
+        if constexpr (f8_of(T)) return launch_shaped<T, D, GMAX, 1, true, PAGED>(p, stream);
         return launch_shaped<T, D, GMAX, 1, false, PAGED>(p, stream);
+    } else if constexpr (f8_of(T)) {
+        return launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream);
     } else {
         return launch_shape(p).prefetch ? launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream)
                                         : launch_shaped<T, D, GMAX, 2, false, PAGED>(p, stream);
