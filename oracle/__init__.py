@@ -33,7 +33,7 @@ class OracleProblem(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("dtype", C.c_int32), ("N", C.c_int32), ("page_size", C.c_int32),
                 ("max_blocks", C.c_int32), ("scale", C.c_double), ("q_dtype", C.c_int32),
-                ("k_scale", C.c_double), ("v_scale", C.c_double)]
+                ("k_scale", C.c_double), ("v_scale", C.c_double), ("q_len", C.c_int32)]
 
 
 def build() -> Path:
@@ -103,14 +103,15 @@ def _i32(a):
 
 
 def problem(B, Hq, Hkv, d, dtype, N=0, page_size=0, max_blocks=0, scale=None, q_dtype=None, k_scale=1.0,
-            v_scale=1.0):
-    """dtype: storage of K and V; q_dtype: storage of q (default: dtype; bf16 for fp8 caches)."""
+            v_scale=1.0, q_len=1):
+    """dtype: storage of K and V; q_dtype: storage of q (default: dtype; bf16 for fp8 caches);
+    q_len query tokens per request (q [B, q_len, Hq, d]; results by row (b*q_len + i)*Hq + h)."""
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     if q_dtype is None:
         q_dtype = "bf16" if dtype == "fp8" else dtype
     return OracleProblem(B, Hq, Hkv, d, DTYPE_CODE[dtype], N, page_size, max_blocks, float(scale),
-                         DTYPE_CODE[q_dtype], float(k_scale), float(v_scale))
+                         DTYPE_CODE[q_dtype], float(k_scale), float(v_scale), int(q_len))
 
 
 def problem_of(inp, scale=None):
@@ -118,7 +119,11 @@ def problem_of(inp, scale=None):
     w = inp.w
     return problem(w.B, w.Hq, w.Hkv, w.d, w.dtype, N=w.N, page_size=w.page_size,
                    max_blocks=w.max_blocks if w.page_size else 0, scale=scale, q_dtype=w.q_dtype,
-                   k_scale=w.k_scale, v_scale=w.v_scale)
+                   k_scale=w.k_scale, v_scale=w.v_scale, q_len=w.q_len)
+
+
+def _nrows(p):
+    return p.B * p.q_len * p.Hq
 
 
 def _rows_arg(rows):
@@ -135,8 +140,8 @@ def attention(p, q, k, v, seq_lens=None, block_table=None, rows=None, threads=No
     q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
-    out = np.full((p.B * p.Hq, p.d), np.nan)
-    lse = np.full(p.B * p.Hq, np.nan)
+    out = np.full((_nrows(p), p.d), np.nan)
+    lse = np.full(_nrows(p), np.nan)
     rc = lib().oracle_attention(C.byref(p), _vp(q), _vp(k), _vp(v), _ptr(sl, C.c_int32), _ptr(bt, C.c_int32),
                                 _ptr(r, C.c_int32), nr, threads or default_threads(),
                                 _ptr(out, C.c_double), _ptr(lse, C.c_double))
@@ -150,7 +155,7 @@ def split_partials(p, q, k, v, split, S_max, seq_lens=None, block_table=None, ro
     q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
-    R = p.B * p.Hq
+    R = _nrows(p)
     po = np.full((R, S_max, p.d), np.nan)
     pm = np.full((R, S_max), np.nan)
     pl = np.full((R, S_max), np.nan)
@@ -204,7 +209,7 @@ def unified_max(p, q, k, v, split, S_max, phi, lo, hi, seq_lens=None, block_tabl
     q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
     r, nr = _rows_arg(rows)
-    R = p.B * p.Hq
+    R = _nrows(p)
     po = np.full((R, S_max, p.d), np.nan)
     pm = np.full((R, S_max), np.nan)
     pl = np.full((R, S_max), np.nan)

@@ -38,6 +38,12 @@
  *   size names KV cache quantization).  The format is OCP FP8 E4M3 (OCP 8-bit
  *   Floating Point Specification, "E4M3"); a stored K or V value means
  *   stored * k_scale or stored * v_scale (one scale per tensor).
+ *   several query tokens per request (verification of drafted tokens, or a
+ *   chunk of new tokens whose K and V are already in the cache): the causal
+ *   mask of the handbook's FlashAttention forward kernel (section
+ *   "FlashAttention: tiling plus online softmax", its causal flag: query
+ *   row i sees keys j <= i), with the q_len new tokens at the last q_len
+ *   positions of the request: query i sees tokens t <= len - q_len + i.
  *
  * Readings taken where the pages leave a step open:
  *   - the last split holds the remainder n - (S-1)*split tokens;
@@ -77,6 +83,7 @@ typedef struct {
     int32_t q_dtype;     /* ODT_F32 / F16 / BF16: storage type of q           */
     double k_scale;      /* a stored K value means stored * k_scale            */
     double v_scale;      /* a stored V value means stored * v_scale            */
+    int32_t q_len;       /* query tokens per request (q is [B][q_len][Hq][d]) */
 } oracle_problem;
 
 /* ---------------------------------------------------------------------- */
@@ -155,6 +162,7 @@ static int check_problem(const oracle_problem *p, const int32_t *seq_lens, const
 {
     if (!p || p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0) return ORACLE_EINVAL;
     if (p->Hq % p->Hkv) return ORACLE_EINVAL;
+    if (p->q_len < 1) return ORACLE_EINVAL;
     if (p->dtype < ODT_F32 || p->dtype > ODT_FP8_E4M3) return ORACLE_EINVAL;
     if (p->q_dtype < ODT_F32 || p->q_dtype > ODT_BF16) return ORACLE_EINVAL;
     if (!(p->k_scale > 0.0) || !(p->v_scale > 0.0) || isinf(p->k_scale) || isinf(p->v_scale))
@@ -170,12 +178,30 @@ static int check_problem(const oracle_problem *p, const int32_t *seq_lens, const
     return ORACLE_OK;
 }
 
-/* scores s_t = scale * <q_h, k_t> for t in [t0, t1), fp64, sequential sums */
+/* Row r = (b * q_len + i) * Hq + h is query token i of request b, head h;
+ * it reads tokens [0, row_tokens) of the request: the causal limit of query
+ * token i, len - q_len + i + 1, clamped to [0, len]. */
+static void row_coords(const oracle_problem *p, int r, int *b, int *h)
+{
+    *b = r / (p->q_len * p->Hq);
+    *h = r % p->Hq;
+}
+
+static int row_tokens(const oracle_problem *p, const int32_t *seq_lens, int r)
+{
+    int b = r / (p->q_len * p->Hq), i = (r / p->Hq) % p->q_len;
+    int n = seq_lens ? seq_lens[b] : p->N;
+    int lim = n - p->q_len + i + 1;
+    lim = lim < 0 ? 0 : lim;
+    return lim < n ? lim : n;
+}
+
+/* scores s_t = scale * <q_r, k_t> for t in [t0, t1), fp64, sequential sums */
 static void scores(const oracle_problem *p, const void *q, const void *k, const int32_t *block_table,
-                   int b, int h, int t0, int t1, double *s)
+                   int r, int b, int h, int t0, int t1, double *s)
 {
     int kvh = h / (p->Hq / p->Hkv);
-    size_t qoff = ((size_t)b * p->Hq + h) * (size_t)p->d;
+    size_t qoff = (size_t)r * (size_t)p->d;
     for (int t = t0; t < t1; ++t) {
         size_t koff = kv_row(p, block_table, b, t, kvh);
         double dot = 0.0;
@@ -211,7 +237,7 @@ static int row_of(const int32_t *rows, int n_rows, int i) { return rows ? rows[i
 
 static int n_rows_total(const oracle_problem *p, const int32_t *rows, int n_rows)
 {
-    return rows ? n_rows : p->B * p->Hq;
+    return rows ? n_rows : p->B * p->q_len * p->Hq;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -229,8 +255,9 @@ int oracle_attention(const oracle_problem *p, const void *q, const void *k, cons
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
     for (int i = 0; i < total; ++i) {
         int r = row_of(rows, n_rows, i);
-        int b = r / p->Hq, h = r % p->Hq;
-        int n = seq_lens ? seq_lens[b] : p->N;
+        int b, h;
+        row_coords(p, r, &b, &h);
+        int n = row_tokens(p, seq_lens, r);
         double *o = out + (size_t)r * p->d;
         if (n == 0) {
             for (int j = 0; j < p->d; ++j) o[j] = 0.0;
@@ -243,7 +270,7 @@ int oracle_attention(const oracle_problem *p, const void *q, const void *k, cons
             failed = 1;
             continue;
         }
-        scores(p, q, k, block_table, b, h, 0, n, s);
+        scores(p, q, k, block_table, r, b, h, 0, n, s);
         double m = s[0];                              /* pass 1: the maximum */
         for (int t = 1; t < n; ++t) m = s[t] > m ? s[t] : m;
         double z = weighted_v(p, v, block_table, b, h, 0, n, s, m, o);   /* pass 2 */
@@ -275,8 +302,9 @@ int oracle_split_partials(const oracle_problem *p, const void *q, const void *k,
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
     for (int i = 0; i < total; ++i) {
         int r = row_of(rows, n_rows, i);
-        int b = r / p->Hq, h = r % p->Hq;
-        int n = seq_lens ? seq_lens[b] : p->N;
+        int b, h;
+        row_coords(p, r, &b, &h);
+        int n = row_tokens(p, seq_lens, r);
         double *s = (double *)malloc((size_t)split * sizeof(double));
         if (!s) {
 #pragma omp atomic write
@@ -293,7 +321,7 @@ int oracle_split_partials(const oracle_problem *p, const void *q, const void *k,
                 for (int j = 0; j < p->d; ++j) o[j] = 0.0;
                 continue;
             }
-            scores(p, q, k, block_table, b, h, t0, t1, s);
+            scores(p, q, k, block_table, r, b, h, t0, t1, s);
             double m = s[0];
             for (int t = 1; t < t1 - t0; ++t) m = s[t] > m ? s[t] : m;
             part_m[slot] = m;
@@ -454,8 +482,9 @@ int oracle_unified_max(const oracle_problem *p, const void *q, const void *k, co
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1) reduction(+ : count)
     for (int i = 0; i < total; ++i) {
         int r = row_of(rows, n_rows, i);
-        int b = r / p->Hq, h = r % p->Hq;
-        int n = seq_lens ? seq_lens[b] : p->N;
+        int b, h;
+        row_coords(p, r, &b, &h);
+        int n = row_tokens(p, seq_lens, r);
         double *s = (double *)malloc((size_t)split * sizeof(double));
         if (!s) {
 #pragma omp atomic write
@@ -473,7 +502,7 @@ int oracle_unified_max(const oracle_problem *p, const void *q, const void *k, co
                 for (int j = 0; j < p->d; ++j) o[j] = 0.0;
                 continue;
             }
-            scores(p, q, k, block_table, b, h, t0, t1, s);
+            scores(p, q, k, block_table, r, b, h, t0, t1, s);
             int bad = 0;
             for (int t = 0; t < t1 - t0; ++t) bad |= oracle_out_of_range(s[t], lo, hi);
             double c = phi;

@@ -162,6 +162,7 @@ class Workload:
     qdtype: Optional[str] = None        # storage of q; None -> dtype (bf16 for an fp8 cache)
     k_scale: float = 1.0                # fp8 caches: a stored K value stands for stored * k_scale
     v_scale: float = 1.0
+    q_len: int = 1                      # query tokens per request: q [B, q_len, Hq, d]
 
     @property
     def q_dtype(self) -> str:
@@ -251,7 +252,7 @@ def make_inputs(w: Workload, poison_tail: bool = True) -> Inputs:
     set to NaN, so that a kernel that reads or weights them shows it.
     """
     lens = seq_lens_for(w)
-    q = normal(SEED_Q, (w.B, w.Hq, w.d), w.q_dtype)
+    q = normal(SEED_Q, (w.B, w.q_len, w.Hq, w.d) if w.q_len > 1 else (w.B, w.Hq, w.d), w.q_dtype)
     table = None
     if w.page_size:
         table, P = block_table_for(w, lens)

@@ -153,6 +153,55 @@ def test_fp8_cache_equals_the_fp32_cache_of_its_values_bitwise():
 
 
 # ----------------------------------------------------------------------------
+# several query tokens per request, causal (the handbook's FlashAttention
+# forward kernel: query row i sees keys j <= i), new tokens at the end
+# ----------------------------------------------------------------------------
+def _multi_query_case(rng, B, q_len, Hq, Hkv, d, N, lens):
+    q = rng.standard_normal((B, q_len, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 2
+    v = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    p = oracle.problem(B, Hq, Hkv, d, "f32", N=N, q_len=q_len)
+    return p, q, k, v, np.asarray(lens, np.int32)
+
+
+def test_multi_query_brute_force_causal():
+    rng = np.random.default_rng(21)
+    B, L, Hq, Hkv, d, N = 2, 3, 2, 1, 4, 6
+    p, q, k, v, lens = _multi_query_case(rng, B, L, Hq, Hkv, d, N, (6, 4))
+    out, lse = oracle.attention(p, q, k, v, seq_lens=lens)
+    for b in range(B):
+        for i in range(L):
+            n = int(lens[b]) - L + i + 1           # query i sits at position len - L + i
+            bo, bl = brute_force(q[b:b + 1, i], k[b:b + 1, :n], v[b:b + 1, :n], None)
+            r0 = (b * L + i) * Hq
+            np.testing.assert_allclose(out[r0:r0 + Hq], bo, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[r0:r0 + Hq], bl, rtol=0, atol=1e-12)
+
+
+def test_multi_query_rows_are_single_queries_with_causal_lengths_bitwise():
+    rng = np.random.default_rng(22)
+    B, L, Hq, Hkv, d, N = 3, 4, 8, 2, 16, 50
+    p, q, k, v, lens = _multi_query_case(rng, B, L, Hq, Hkv, d, N, (50, 9, 2))
+    out, lse = oracle.attention(p, q, k, v, seq_lens=lens)
+    po, pm, pl = oracle.split_partials(p, q, k, v, 8, 7, seq_lens=lens)
+    for b in range(B):
+        for i in range(L):
+            n = max(0, int(lens[b]) - L + i + 1)
+            p1 = oracle.problem(1, Hq, Hkv, d, "f32", N=N)
+            o1, l1 = oracle.attention(p1, q[b, i][None], k[b:b + 1], v[b:b + 1], seq_lens=np.array([n], np.int32))
+            a1, m1, s1 = oracle.split_partials(p1, q[b, i][None], k[b:b + 1], v[b:b + 1], 8, 7,
+                                               seq_lens=np.array([n], np.int32))
+            r = slice((b * L + i) * Hq, (b * L + i + 1) * Hq)
+            assert np.array_equal(out[r], o1) and np.array_equal(lse[r], l1)
+            assert np.array_equal(pm[r], m1) and np.array_equal(pl[r], s1)
+            valid = s1 > 0
+            assert np.array_equal(po[r][valid], a1[valid])
+    # a query before the start of its request sees nothing
+    r = (2 * L + 0) * Hq
+    assert np.all(out[r:r + Hq] == 0.0) and np.all(lse[r:r + Hq] == -np.inf)
+
+
+# ----------------------------------------------------------------------------
 # the handbook's worked online-softmax exercise
 # ----------------------------------------------------------------------------
 def test_worked_exercise_attention(golden):
