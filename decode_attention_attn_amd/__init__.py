@@ -38,15 +38,15 @@ class fd_decode_desc(C.Structure):
                 ("kv_dtype", C.c_int32), ("out_dtype", C.c_int32), ("split_size", C.c_int32),
                 ("max_splits", C.c_int32), ("scale", C.c_float), ("mode", C.c_int32),
                 ("phi", C.c_float), ("lo", C.c_float), ("hi", C.c_float), ("kernel", C.c_int32),
-                ("q_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
+                ("q_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float), ("q_len", C.c_int32)]
 
 
 def make_desc(B, Hq, Hkv, d, kv_dtype="bf16", out_dtype=None, split_size=256, max_splits=None,
               max_seq_len=None, scale=0.0, mode="sync", phi=0.0, lo=0.0, hi=0.0, kernel="auto", q_dtype=None,
-              k_scale=0.0, v_scale=0.0):
+              k_scale=0.0, v_scale=0.0, q_len=1):
     """Descriptor with names instead of enum codes.  max_splits defaults to
     ceil(max_seq_len / split_size); q_dtype (8-bit caches only) defaults to
-    bf16, and out_dtype to the type of q."""
+    bf16, and out_dtype to the type of q.  q_len: causal query tokens per request."""
     if max_splits is None:
         if max_seq_len is None:
             raise ValueError("give max_splits or max_seq_len")
@@ -56,7 +56,7 @@ def make_desc(B, Hq, Hkv, d, kv_dtype="bf16", out_dtype=None, split_size=256, ma
     return fd_decode_desc(int(B), int(Hq), int(Hkv), int(d), DTYPES[kv_dtype],
                           DTYPES[out_dtype or q_dtype], int(split_size), int(max_splits), float(scale),
                           MODES[mode], float(phi), float(lo), float(hi), KERNELS[kernel], DTYPES[q_dtype],
-                          float(k_scale), float(v_scale))
+                          float(k_scale), float(v_scale), int(q_len))
 
 
 _lib = None
@@ -158,9 +158,14 @@ def _check(fn, st):
         raise FdError(fn, st)
 
 
+def query_rows(desc):
+    """Query rows per request: q_len * Hq."""
+    return max(1, desc.q_len) * desc.Hq
+
+
 def partial_shapes(desc):
     """Shapes of (part_o, part_m, part_l, flags) for a descriptor."""
-    rows = (desc.B, desc.Hq, desc.max_splits)
+    rows = (desc.B, query_rows(desc), desc.max_splits)
     return rows + (desc.d,), rows, rows, rows
 
 
@@ -169,9 +174,9 @@ def fd_decode_attn_partial(desc, q, k, v, kv_capacity, seq_lens, part_o, part_m,
     """Split partials over a contiguous cache k, v [B, kv_capacity, Hkv, d]."""
     torch = _torch()
     kvt = _tdtype(desc.kv_dtype)
-    nrow = desc.B * desc.Hq * desc.max_splits
+    nrow = desc.B * query_rows(desc) * desc.max_splits
     args = [
-        _ptr(q, "q", _qdtype(desc), desc.B * desc.Hq * desc.d),
+        _ptr(q, "q", _qdtype(desc), desc.B * query_rows(desc) * desc.d),
         _ptr(k, "k", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         _ptr(v, "v", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         C.c_int32(int(kv_capacity)),
@@ -188,14 +193,14 @@ def fd_decode_attn_partial(desc, q, k, v, kv_capacity, seq_lens, part_o, part_m,
 
 def fd_decode_attn_combine(desc, part_o, part_m, part_l, seq_lens, out, lse=None, stream=None):
     torch = _torch()
-    nrow = desc.B * desc.Hq * desc.max_splits
+    nrow = desc.B * query_rows(desc) * desc.max_splits
     args = [
         _ptr(part_o, "part_o", torch.float32, nrow * desc.d),
         _ptr(part_m, "part_m", torch.float32, nrow),
         _ptr(part_l, "part_l", torch.float32, nrow),
         _ptr(seq_lens, "seq_lens", torch.int32, desc.B, optional=True),
-        _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * desc.Hq * desc.d),
-        _ptr(lse, "lse", torch.float32, desc.B * desc.Hq, optional=True),
+        _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * query_rows(desc) * desc.d),
+        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True),
         _stream(stream),
     ]
     _check("fd_decode_attn_combine", lib().fd_decode_attn_combine(C.byref(desc), *args))
@@ -213,12 +218,12 @@ def fd_decode_attn_paged(desc, q, k_cache, v_cache, page_size, block_table, seq_
     if block_table.dim() != 2 or block_table.shape[0] != desc.B:
         raise ValueError("block_table must be [B, max_blocks_per_seq]")
     num_pages = int(k_cache.shape[0])
-    nrow = desc.B * desc.Hq * desc.max_splits
+    nrow = desc.B * query_rows(desc) * desc.max_splits
     ws_bytes = fd_workspace_bytes(desc)
     if workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError(f"workspace needs {ws_bytes} bytes")
     args = [
-        _ptr(q, "q", _qdtype(desc), desc.B * desc.Hq * desc.d),
+        _ptr(q, "q", _qdtype(desc), desc.B * query_rows(desc) * desc.d),
         _ptr(k_cache, "k_cache", kvt),
         _ptr(v_cache, "v_cache", kvt),
         C.c_int32(num_pages), C.c_int32(int(page_size)),
@@ -227,8 +232,8 @@ def fd_decode_attn_paged(desc, q, k_cache, v_cache, page_size, block_table, seq_
         _ptr(seq_lens, "seq_lens", torch.int32, desc.B),
         _ptr(workspace, "workspace"),
         C.c_size_t(workspace.numel() * workspace.element_size()),
-        _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * desc.Hq * desc.d),
-        _ptr(lse, "lse", torch.float32, desc.B * desc.Hq, optional=True),
+        _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * query_rows(desc) * desc.d),
+        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True),
         _ptr(flags, "flags", torch.uint8, nrow, optional=True),
         _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True),
         _stream(stream),

@@ -22,6 +22,8 @@ fd_status validate_desc(const fd_decode_desc *d) {
     if (d->B < 0 || d->B > 65535 || d->Hq <= 0 || d->Hkv <= 0 || d->Hkv > 65535) return FD_ERR_INVALID_ARG;
     if (d->Hq % d->Hkv) return FD_ERR_INVALID_ARG;
     if (d->Hq / d->Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
+    if (d->q_len > kMaxGroup || (int64_t)(d->q_len > 1 ? d->q_len : 1) * (d->Hq / d->Hkv) > kMaxGroup)
+        return FD_ERR_UNSUPPORTED;   // a KV head's query rows must fit one 16-row matrix tile
     if (d->d != 64 && d->d != 128) return FD_ERR_UNSUPPORTED;
     if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
     if (d->kv_dtype == FD_FP8_E4M3) {
@@ -65,6 +67,8 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     p.Hq = d->Hq;
     p.Hkv = d->Hkv;
     p.G = d->Hq / d->Hkv;
+    p.q_len = d->q_len > 1 ? d->q_len : 1;
+    p.R = p.q_len * p.G;
     p.d = d->d;
     p.split = d->split_size;
     p.max_splits = d->max_splits;
@@ -106,7 +110,7 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout layout(const fd_decode_desc *d) {
-    const size_t rows = (size_t)d->B * d->Hq * d->max_splits;
+    const size_t rows = (size_t)d->B * (d->q_len > 1 ? d->q_len : 1) * d->Hq * d->max_splits;
     WorkspaceLayout w;
     w.o_bytes = round256(rows * d->d * sizeof(float));
     w.m_bytes = round256(rows * sizeof(float));
@@ -124,7 +128,7 @@ fd_status run_combine(const fd_decode_desc *d, const float *part_o, const float 
     c.out = out;
     c.lse = lse;
     c.B = d->B;
-    c.Hq = d->Hq;
+    c.Hq = (d->q_len > 1 ? d->q_len : 1) * d->Hq;   // query rows per request
     c.d = d->d;
     c.split = d->split_size;
     c.max_splits = d->max_splits;

@@ -174,6 +174,25 @@ __device__ __forceinline__ int split_index(int x, int b, int kvh, int Hkv, int S
     return (int)(((unsigned)x + (unsigned)(b * Hkv + kvh)) % (unsigned)S);
 }
 
+// Query row rho < R of KV head kvh in request b: query token i = rho / G of
+// head kvh * G + rho % G.  Its global row (b * q_len + i) * Hq + head indexes
+// q, out and lse; its split slot indexes the partials and flags.
+__device__ __forceinline__ size_t query_row(const PartialParams &p, int b, int kvh, int rho) {
+    const int i = rho / p.G, g = rho - i * p.G;
+    return ((size_t)b * p.q_len + i) * p.Hq + (size_t)kvh * p.G + g;
+}
+
+__device__ __forceinline__ size_t row_slot(const PartialParams &p, int b, int kvh, int rho, int s) {
+    return query_row(p, b, kvh, rho) * p.max_splits + s;
+}
+
+// Causal limit of query row rho inside the split ending at t1: query token i
+// sits at position len - q_len + i and sees the tokens up to it.
+__device__ __forceinline__ int row_limit(const PartialParams &p, int len, int t1, int rho) {
+    const int lim = len - p.q_len + rho / p.G + 1;
+    return lim < t1 ? lim : t1;
+}
+
 // Number of tokens of request b that the kernels read.
 __device__ __forceinline__ int request_len(const int32_t *seq_lens, int b, int cap, int limit) {
     int n = seq_lens ? seq_lens[b] : cap;

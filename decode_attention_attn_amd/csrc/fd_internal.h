@@ -32,6 +32,8 @@ struct PartialParams {
     uint8_t *flags;             // [B, Hq, S_max] or nullptr
     int32_t *fallback_count;    // [1] or nullptr
     int32_t B, Hq, Hkv, G, d;
+    int32_t q_len;              // query tokens per request (causal)
+    int32_t R;                  // query rows per KV head: q_len * G (<= 16)
     int32_t kv_capacity;        // contiguous: tokens per request row; paged: max_blocks * page
     int32_t page_size;          // 0 = contiguous
     int32_t max_blocks;
@@ -51,7 +53,7 @@ struct CombineParams {
     const int32_t *seq_lens;
     void *out;                  // [B, Hq, d]
     float *lse;                 // [B, Hq] or nullptr
-    int32_t B, Hq, d;
+    int32_t B, Hq, d;           // Hq: query rows per request (q_len * heads)
     int32_t split, max_splits;
     int32_t out_dtype;
 };

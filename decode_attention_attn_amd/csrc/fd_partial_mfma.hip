@@ -280,8 +280,9 @@ __device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi)
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// lim: this lane's query row (lane % 16) sees tokens < lim of the split
 template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int t1,
+__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int lim,
                                               const uint4 (&kr)[KLoad<T, D>::LI],
                                               const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
                                               MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
@@ -324,7 +325,7 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const bool ok = br.page_ok && br.tb + 4 * mq + r < t1;
+        const bool ok = br.page_ok && br.tb + 4 * mq + r < lim;
         s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
     }
 
@@ -390,7 +391,7 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
 // split's block-table entries once (one per lane) and pick each block's page
 // from them with a lane read.
 template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const uint4 (&qop)[D / 32],
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, int lim, const uint4 (&qop)[D / 32],
                            MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using L = KLoad<T, D>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -415,25 +416,25 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
         for (; j + 2 < n; j += 2) {
             rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
             load_block<T, D>(p, rb, t1, off, kb2, vb2);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
             ra = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 2) * tstep, t1);
             load_block<T, D>(p, ra, t1, off, ka, va);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
         }
         if (j + 2 == n) {
             rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
             load_block<T, D>(p, rb, t1, off, kb2, vb2);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, t1, kb2, vb2, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
         } else {
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, t1, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
         }
     } else {
         for (int blk = wave; blk < nblk; blk += WAVES) {
             const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
             uint4 kr[L::LI], vr[L::LI];
             load_block<T, D>(p, br, t1, off, kr, vr);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, br, t1, kr, vr, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, kr, vr, qop, st, sm);
         }
     }
 }
@@ -443,8 +444,8 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 // one dim per slice, one 16-byte LDS store each); after one barrier each
 // thread merges one dim of four heads over the waves by the max-rescale rule.
 template <int T, int D, int GMAX, int WAVES>
-__device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, size_t slot0,
-                             uint32_t write_mask) {
+__device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
+                             int s, uint32_t write_mask) {
     using C = MCfg<D, GMAX, WAVES>;
     constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -496,8 +497,8 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int g = 4 * gq + r;
-            if (g >= p.G || !((write_mask >> g) & 1u)) continue;
-            const size_t slot = slot0 + (size_t)g * p.max_splits;
+            if (g >= p.R || !((write_mask >> g) & 1u)) continue;
+            const size_t slot = row_slot(p, b, kvh, g, s);
             float o = L[r] > 0.f ? a4[r] / L[r] : 0.f;
             if constexpr (f8_of(T)) o *= p.v_mult;   // a stored V unit stands for v_scale
             p.part_o[slot * D + dim] = o;
@@ -517,15 +518,14 @@ partial_mfma_kernel(const PartialParams p) {
     __shared__ MSmem<D, GMAX, WAVES> sm;
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
-    const int G = p.G, h0 = kvh * G;
+    const int R = p.R;                               // query rows of this KV head
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
     const int t0 = s * p.split;
     const int t1 = min(t0 + p.split, len);
-    const size_t slot0 = ((size_t)b * p.Hq + h0) * p.max_splits + s;
 
     if (t0 >= t1) {
-        if (threadIdx.x < G) {
-            const size_t slot = slot0 + (size_t)threadIdx.x * p.max_splits;
+        if (threadIdx.x < R) {
+            const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
             p.part_m[slot] = -INFINITY;
             p.part_l[slot] = 0.f;
             if (p.flags) p.flags[slot] = 0;
@@ -534,25 +534,26 @@ partial_mfma_kernel(const PartialParams p) {
     }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // B operand: q of head (lane % 16) of the group, dims 8 * (lane / 16) of each step
+    // B operand: q of query row (lane % 16), dims 8 * (lane / 16) of each step
     uint4 qop[C::KS];
+    const int lim = row_limit(p, len, t1, lane & 15);
     {
-        const int g = lane & 15;
+        const int rho = lane & 15;
         const char *qb = static_cast<const char *>(p.q);
+        const size_t qrow = rho < R ? query_row(p, b, kvh, rho) : 0;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             qop[ks] = make_uint4(0, 0, 0, 0);
-            if (g < G)
-                qop[ks] = load16(qb + (((size_t)b * p.Hq + h0 + g) * D + 32 * ks + 8 * (lane >> 4)) * 2);
+            if (rho < R) qop[ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
         }
     }
 
-    const uint32_t all = (1u << G) - 1u;
+    const uint32_t all = (1u << R) - 1u;
     MState<D, GMAX> st;
     uint32_t badmask = 0;
     if constexpr (UNI) {
         st.init(p.phi2);
-        scan_split<T, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, qop, st, sm);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
         const uint64_t bal = __ballot(st.bad);
         const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
         if (lane == 0) sm.bad[wave] = mine;
@@ -560,22 +561,21 @@ partial_mfma_kernel(const PartialParams p) {
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
         badmask &= all;
-        finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, all & ~badmask);
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all & ~badmask);
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
-            finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, badmask);
+            scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+            finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, badmask);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, qop, st, sm);
-        finish_split<T, D, GMAX, WAVES>(p, st, sm, slot0, all);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all);
     }
-    if (p.flags && threadIdx.x < G)
-        p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
+    if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
 
 // Launch shape: waves per workgroup and whether a wave prefetches its next
@@ -591,7 +591,7 @@ Shape launch_shape(const PartialParams &p) {
     const bool f8 = p.dtype == FP8;
     // groups of more than four heads: one wave per workgroup (B=4, N=128k,
     // G=8 and B=64 paged batches measured no slower than with two)
-    if (p.G > 4) return Shape{1, f8};
+    if (p.R > 4) return Shape{1, f8};
     // fewer than four workgroups per CU: each SIMD runs one or two waves and a
     // wave's own load-then-compute chain sets the pace, so overlap the two
     // (Llama-2-7B-shaped MHA, 512 workgroups: 14.7 us against 15.5 us)
@@ -633,10 +633,10 @@ hipError_t by_paged(const PartialParams &p, hipStream_t s) {
 
 template <int T, int D>
 hipError_t by_group(const PartialParams &p, hipStream_t s) {
-    if (p.G <= 1) return by_paged<T, D, 1>(p, s);
-    if (p.G <= 2) return by_paged<T, D, 2>(p, s);
-    if (p.G <= 4) return by_paged<T, D, 4>(p, s);
-    if (p.G <= 8) return by_paged<T, D, 8>(p, s);
+    if (p.R <= 1) return by_paged<T, D, 1>(p, s);
+    if (p.R <= 2) return by_paged<T, D, 2>(p, s);
+    if (p.R <= 4) return by_paged<T, D, 4>(p, s);
+    if (p.R <= 8) return by_paged<T, D, 8>(p, s);
     return by_paged<T, D, 16>(p, s);
 }
 

@@ -76,8 +76,9 @@ __device__ __forceinline__ size_t row_offset(const PartialParams &p, int b, int 
     return row * D;
 }
 
+// lim[g]: query row g sees tokens < lim[g] of the split (causal rows)
 template <int DT, int D, int GMAX, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1,
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const int (&lim)[GMAX],
                            const float (&qv)[GMAX][Cfg<DT, D, GMAX>::E], State<DT, D, GMAX> &st) {
     using C = Cfg<DT, D, GMAX>;
     constexpr int E = C::E, LPR = C::LPR, RPW = C::RPW, R = C::R;
@@ -89,9 +90,11 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     for (int tb = t0; tb < t1; tb += C::TOK_STEP) {
         uint4 kr[R], vr[R];
         bool ok[R];
+        int tok[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int t = tb + (wave * R + r) * RPW + rg;
+            tok[r] = t;
             ok[r] = t < t1;
             const size_t off = (row_offset<PAGED, D>(p, b, kvh, ok[r] ? t : t0, ok[r]) + (size_t)c * E) * C::BYTES;
             kr[r] = ok[r] ? load_piece<DT>(kb + off) : make_uint4(0, 0, 0, 0);
@@ -108,7 +111,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 #pragma unroll
                 for (int e = 0; e < E; ++e) dot = fmaf(qv[g][e], kf[e], dot);
                 dot = group_sum<LPR>(dot);
-                s[r][g] = ok[r] ? dot * p.scale_log2 : -INFINITY;
+                s[r][g] = (ok[r] && tok[r] < lim[g]) ? dot * p.scale_log2 : -INFINITY;
             }
         }
         float vf[R][E];
@@ -120,7 +123,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
             if constexpr (UNIFIED) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    st.bad[g] = st.bad[g] || (ok[r] && (s[r][g] < p.lo2 || s[r][g] > p.hi2));
+                    st.bad[g] = st.bad[g] || (s[r][g] != -INFINITY && (s[r][g] < p.lo2 || s[r][g] > p.hi2));
                 mref = p.phi2;
             } else {
                 float mt = s[0][g];
@@ -178,8 +181,8 @@ struct Smem {
 
 // Wave states -> LDS -> the split's partial for the heads in `write_mask`.
 template <int DT, int D, int GMAX>
-__device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Smem<D, GMAX> &sm,
-                             size_t slot0, uint32_t write_mask) {
+__device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Smem<D, GMAX> &sm, int b, int kvh,
+                             int s, uint32_t write_mask) {
     using C = Cfg<DT, D, GMAX>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     merge_wave(st);
@@ -195,7 +198,7 @@ __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Sme
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < p.G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < p.R * D; idx += kThreads) {
         const int g = idx / D, dim = idx % D;
         if (!((write_mask >> g) & 1u)) continue;
         float mm = sm.m[0][g];
@@ -208,7 +211,7 @@ __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Sme
             L += sm.l[w][g] * f;
             A += sm.acc[w][g][dim] * f;
         }
-        const size_t slot = slot0 + (size_t)g * p.max_splits;
+        const size_t slot = row_slot(p, b, kvh, g, s);
         float o = L > 0.f ? A / L : 0.f;
         if constexpr (DT == FP8) o *= p.v_mult;
         p.part_o[slot * D + dim] = o;
@@ -227,15 +230,14 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
-    const int G = p.G, h0 = kvh * G;
+    const int G = p.R;                               // query rows of this KV head
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
     const int t0 = s * p.split;
     const int t1 = min(t0 + p.split, len);
-    const size_t slot0 = ((size_t)b * p.Hq + h0) * p.max_splits + s;
 
     if (t0 >= t1) {   // empty split: nothing to read
         if (threadIdx.x < G) {
-            const size_t slot = slot0 + (size_t)threadIdx.x * p.max_splits;
+            const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
             p.part_m[slot] = -INFINITY;
             p.part_l[slot] = 0.f;
             if (p.flags) p.flags[slot] = 0;
@@ -246,18 +248,21 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % C::LPR;
     float qv[GMAX][E];
+    int lim[GMAX];
     const char *qb = static_cast<const char *>(p.q);
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
+        lim[g] = row_limit(p, len, t1, g);
         if (g < G) {
+            const size_t qrow = query_row(p, b, kvh, g);
             if constexpr (DT == FP8) {   // q is f16 or bf16
-                const uint4 raw = load16(qb + (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * 2);
+                const uint4 raw = load16(qb + (qrow * D + (size_t)c * E) * 2);
                 if (p.q_dtype == BF16)
                     unpack<BF16>(raw, qv[g]);
                 else
                     unpack<F16>(raw, qv[g]);
             } else {
-                const size_t off = (((size_t)b * p.Hq + h0 + g) * D + (size_t)c * E) * C::BYTES;
+                const size_t off = (qrow * D + (size_t)c * E) * C::BYTES;
                 unpack<DT>(load16(qb + off), qv[g]);
             }
         } else {
@@ -271,7 +276,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     uint32_t badmask = 0;
     if (p.unified) {
         st.init(p.phi2);
-        scan_split<DT, D, GMAX, PAGED, true>(p, b, kvh, t0, t1, qv, st);
+        scan_split<DT, D, GMAX, PAGED, true>(p, b, kvh, t0, t1, lim, qv, st);
         uint32_t mine = 0;
 #pragma unroll
         for (int g = 0; g < GMAX; ++g)
@@ -281,22 +286,21 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) badmask |= sm.bad[w];
         badmask &= all;
-        finish_split<DT, D, GMAX>(p, st, sm, slot0, all & ~badmask);
+        finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, all & ~badmask);
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, qv, st);
-            finish_split<DT, D, GMAX>(p, st, sm, slot0, badmask);
+            scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, lim, qv, st);
+            finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, badmask);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, qv, st);
-        finish_split<DT, D, GMAX>(p, st, sm, slot0, all);
+        scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, lim, qv, st);
+        finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, all);
     }
-    if (p.flags && threadIdx.x < G)
-        p.flags[slot0 + (size_t)threadIdx.x * p.max_splits] = (badmask >> threadIdx.x) & 1u;
+    if (p.flags && threadIdx.x < G) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
 
 template <int DT, int D, int GMAX, bool PAGED>
@@ -313,10 +317,10 @@ hipError_t by_paged(const PartialParams &p, hipStream_t s) {
 
 template <int DT, int D>
 hipError_t by_group(const PartialParams &p, hipStream_t s) {
-    if (p.G <= 1) return by_paged<DT, D, 1>(p, s);
-    if (p.G <= 2) return by_paged<DT, D, 2>(p, s);
-    if (p.G <= 4) return by_paged<DT, D, 4>(p, s);
-    if (p.G <= 8) return by_paged<DT, D, 8>(p, s);
+    if (p.R <= 1) return by_paged<DT, D, 1>(p, s);
+    if (p.R <= 2) return by_paged<DT, D, 2>(p, s);
+    if (p.R <= 4) return by_paged<DT, D, 4>(p, s);
+    if (p.R <= 8) return by_paged<DT, D, 8>(p, s);
     return by_paged<DT, D, 16>(p, s);
 }
 

@@ -21,8 +21,18 @@
  *    up at the caller's next synchronisation, not in the status.
  *  - Tensors are dense, row-major, with 16-byte aligned base pointers; offsets
  *    are computed in 64 bits.
- *  - q has shape [B, Hq, d] and the same element type as the cache, except
- *    with an 8-bit cache, where q is f16 or bf16 (desc->q_dtype).
+ *  - q has shape [B, q_len, Hq, d] ([B, Hq, d] for q_len = 1) and the same
+ *    element type as the cache, except with an 8-bit cache, where q is f16 or
+ *    bf16 (desc->q_dtype).
+ *  - Query rows: r = (b * q_len + i) * Hq + h is query token i of request b,
+ *    head h.  With q_len > 1 (drafted tokens to verify, or a chunk of new
+ *    tokens whose K and V are already in the cache) the q_len tokens are the
+ *    last q_len positions of the request and attend causally: token i sees
+ *    cache tokens t <= len_b - q_len + i (the causal mask of the handbook's
+ *    FlashAttention forward kernel, page "FlashAttention and inference
+ *    kernels", section "FlashAttention: tiling plus online softmax").  Every
+ *    per-head shape below is per query row: out [B, q_len, Hq, d], lse, m, l
+ *    and flags [B, q_len, Hq, ...].  q_len * (Hq / Hkv) <= 16.
  *  - 8-bit caches (FD_FP8_E4M3, OCP FP8 E4M3: bias 7, no infinities, largest
  *    finite 448, S.1111.111 = NaN) stand for stored * k_scale and
  *    stored * v_scale (one scale per tensor); the handbook page lists caches
@@ -40,12 +50,13 @@
  *  - Split s of request b covers tokens [s * split_size, min((s+1) * split_size,
  *    len_b)); the last split holds the remainder.  A split with no tokens
  *    reports m = -inf, l = 0 and leaves its O row unwritten.
- *  - Partials (fp32): part_o [B, Hq, max_splits, d] holds the split's output
- *    already divided by its l; part_m, part_l [B, Hq, max_splits] hold the
+ *  - Partials (fp32): part_o [B, q_len, Hq, max_splits, d] holds the split's
+ *    output already divided by its l; part_m, part_l [B, q_len, Hq, max_splits]
+ *    hold the
  *    split's scaling constant m (natural-log units of scaled scores) and
  *    l = sum_t exp(s_t - m).
- *  - lse (fp32 [B, Hq]) = ln sum_t exp(s_t) with s_t = scale * <q, k_t>;
- *    -inf for an empty request, whose out row is 0.
+ *  - lse (fp32 [B, q_len, Hq]) = ln sum_t exp(s_t) with s_t = scale * <q, k_t>;
+ *    -inf for a row that sees no token, whose out row is 0.
  *  - Results are bitwise repeatable run to run (no floating-point atomics).
  *  - Errors are returned, never thrown; on error nothing is enqueued.
  */
@@ -107,12 +118,13 @@ typedef struct fd_decode_desc {
                                 ignored otherwise (q has kv_dtype) */
     float k_scale, v_scale;  /* FD_FP8_E4M3 caches: a stored K / V value stands for
                                 stored * scale; <= 0 selects 1; ignored otherwise */
+    int32_t q_len;           /* query tokens per request, causal; <= 0 selects 1 */
 } fd_decode_desc;
 
 /* Split-partial kernel over a contiguous cache.
  *   k, v          : [B, kv_capacity, Hkv, d] of kv_dtype
  *   part_o/m/l    : as in the conventions above (written for every split < max_splits)
- *   flags         : uint8 [B, Hq, max_splits] or NULL; UNIFIED_MAX writes 1 for a
+ *   flags         : uint8 [B, q_len, Hq, max_splits] or NULL; UNIFIED_MAX writes 1 for a
  *                   (request, query head, split) whose scores left [lo, hi], else 0
  *   fallback_count: int32 [1] or NULL; UNIFIED_MAX adds the number of flagged
  *                   (request, query head, split) triples (set it to 0 first for
@@ -130,7 +142,7 @@ fd_status fd_decode_attn_partial(const fd_decode_desc *desc, const void *q, cons
  * and Online Softmax Reduction Algorithm"; empty splits skipped as in the
  * handbook's split-K merge exercise).  Request b reads splits
  * s < ceil(len_b / split_size) (all max_splits when seq_lens is NULL; then
- * kv_capacity is unused).  out: [B, Hq, d] of out_dtype; lse: fp32 [B, Hq] or NULL. */
+ * kv_capacity is unused).  out: [B, q_len, Hq, d] of out_dtype; lse: fp32 [B, q_len, Hq] or NULL. */
 fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float *part_o, const float *part_m,
                                  const float *part_l, const int32_t *seq_lens, void *out, float *lse,
                                  void *stream);

@@ -194,6 +194,9 @@ WORKLOADS = {
     # the long-context GQA shape with an 8-bit cache (scale 1/64: N(0, 1) draws stored as 64 x)
     "long_gqa_32k_fp8": Workload("long_gqa_32k_fp8", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256,
                                  N=32768, k_scale=1.0 / 64, v_scale=1.0 / 64),
+    # the long-context GQA shape verifying 4 drafted tokens (4 x 4 query rows per KV head)
+    "long_gqa_32k_verify4": Workload("long_gqa_32k_verify4", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256,
+                                     N=32768, q_len=4),
 }
 
 

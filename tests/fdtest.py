@@ -61,7 +61,8 @@ def assert_close(got, ref, dtype, what, atol=None, rtol=None):
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     both_inf = np.isinf(ref) & (got == ref)
-    err = np.where(both_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):          # inf - inf where both are -inf: masked below
+        err = np.where(both_inf, 0.0, np.abs(got - ref))
     bound = atol + rtol * np.where(np.isinf(ref), 0.0, np.abs(ref))
     bad = ~(err <= bound)
     if bad.any():
@@ -93,7 +94,7 @@ class Run:
         f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
         return fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, out_dtype, split_size=split,
                             max_splits=max_splits or max(1, -(-w.N // split)), mode=mode, phi=phi, lo=lo,
-                            hi=hi, kernel=kernel, **f8)
+                            hi=hi, kernel=kernel, q_len=w.q_len, **f8)
 
     def run(self, use_lens=True, **kw):
         """Partial + combine (contiguous) or the paged entry point.  Returns a dict
@@ -102,28 +103,29 @@ class Run:
         w = self.w
         desc = self.desc(**kw)
         S = desc.max_splits
-        out = t.empty((w.B, w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device="cuda")
-        lse = t.empty((w.B, w.Hq), dtype=t.float32, device="cuda")
-        flags = t.full((w.B, w.Hq, S), 7, dtype=t.uint8, device="cuda")
+        QR = w.q_len * w.Hq                  # query rows per request
+        out = t.empty((w.B, QR, w.d), dtype=fd._tdtype(desc.out_dtype), device="cuda")
+        lse = t.empty((w.B, QR), dtype=t.float32, device="cuda")
+        flags = t.full((w.B, QR, S), 7, dtype=t.uint8, device="cuda")
         count = t.zeros(1, dtype=t.int32, device="cuda")
         lens = self.lens if use_lens else None
         if w.page_size:
             ws = fd.alloc_workspace(desc)
             fd.fd_decode_attn_paged(desc, self.q, self.k, self.v, w.page_size, self.table, self.lens, ws, out,
                                     lse, flags, count)
-            n = w.B * w.Hq * S
+            n = w.B * QR * S
             o_bytes = (n * w.d * 4 + 255) // 256 * 256
             m_bytes = (n * 4 + 255) // 256 * 256
             fw = ws.view(t.float32)
-            po = fw[:n * w.d].view(w.B, w.Hq, S, w.d)
-            pm = fw[o_bytes // 4:o_bytes // 4 + n].view(w.B, w.Hq, S)
-            pl = fw[(o_bytes + m_bytes) // 4:(o_bytes + m_bytes) // 4 + n].view(w.B, w.Hq, S)
+            po = fw[:n * w.d].view(w.B, QR, S, w.d)
+            pm = fw[o_bytes // 4:o_bytes // 4 + n].view(w.B, QR, S)
+            pl = fw[(o_bytes + m_bytes) // 4:(o_bytes + m_bytes) // 4 + n].view(w.B, QR, S)
         else:
             po, pm, pl, _ = fd.alloc_partials(desc)
             fd.fd_decode_attn_partial(desc, self.q, self.k, self.v, w.N, lens, po, pm, pl, flags, count)
             fd.fd_decode_attn_combine(desc, po, pm, pl, lens, out, lse)
         t.cuda.synchronize()
-        R = w.B * w.Hq
+        R = w.B * QR
         return dict(out=f64(out).reshape(R, w.d), lse=f64(lse).reshape(R),
                     part_o=f64(po).reshape(R, S, w.d), part_m=f64(pm).reshape(R, S),
                     part_l=f64(pl).reshape(R, S), flags=flags.cpu().numpy().reshape(R, S),
@@ -175,7 +177,7 @@ def flag_bounds(inp, split, S, phi, lo, hi, rows=None):
 
 
 def sample_rows(w, n, seed=0):
-    R = w.B * w.Hq
+    R = w.B * w.q_len * w.Hq
     if n >= R:
         return np.arange(R, dtype=np.int32)
     rng = np.random.default_rng(seed)

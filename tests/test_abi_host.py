@@ -186,6 +186,18 @@ def test_fp8_descriptor_validation():
     assert fd.fd_workspace_bytes(ok) == fd.fd_workspace_bytes(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4))
 
 
+def test_multi_query_descriptor_validation():
+    """q_len * (Hq / Hkv) query rows of a KV head must fit one 16-row tile."""
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=4)) == fd.FD_ERR_INVALID_ARG
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=5)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=17)) == fd.FD_ERR_UNSUPPORTED
+    one = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4)
+    zero = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=0)
+    four = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=4)
+    assert fd.fd_workspace_bytes(zero) == fd.fd_workspace_bytes(one)
+    assert fd.fd_workspace_bytes(four) >= 4 * fd.fd_workspace_bytes(one) - 3 * 256 * 3
+
+
 def test_empty_batch_is_a_no_op():
     desc = fd.make_desc(0, 8, 8, 128, "bf16", max_splits=4)
     assert _partial_status(desc) == fd.FD_OK

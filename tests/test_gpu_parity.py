@@ -502,3 +502,79 @@ def test_fp8_long_context_gqa_full():
     e1, e2 = ft.check_exact(res, inp, what="long_gqa_32k_fp8")
     ft.check_partials(res, inp, w.split, what="long_gqa_32k_fp8")
     say(f"[long_gqa_32k_fp8] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+
+
+# ----------------------------------------------------------------------------
+# several causal query tokens per request (draft verification / a chunk of new
+# tokens already in the cache); q_len * G rows share one KV head
+# ----------------------------------------------------------------------------
+MQ_CASES = [  # (kernel, dtype, Hq, Hkv, q_len)
+    ("mfma", "bf16", 32, 8, 4), ("mfma", "bf16", 8, 8, 16), ("mfma", "f16", 16, 8, 8), ("mfma", "bf16", 24, 8, 5),
+    ("mfma", "fp8", 32, 8, 4), ("valu", "f32", 16, 8, 3), ("valu", "bf16", 32, 8, 4), ("valu", "fp8", 8, 8, 2),
+]
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len", MQ_CASES)
+def test_multi_query_causal(kernel, dtype, Hq, Hkv, q_len, page):
+    extra = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if dtype == "fp8" else {}
+    base = synth.Workload("mq", B=1, Hq=Hq, Hkv=Hkv, d=128, dtype=dtype, split=128, N=1, page_size=page,
+                          q_len=q_len, **extra)
+    # lengths cover a split boundary inside the query window and a request
+    # shorter than its query tokens
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 129, 130, 3, 2 * q_len)))
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel))
+    what = f"q_len={q_len} {kernel} {dtype} G={Hq // Hkv} page={page}"
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 128, what=what)
+    # query token 0 of the request of length 3 < q_len sees nothing when q_len > 3
+    if q_len > 3:
+        r0 = (3 * q_len + 0) * Hq
+        assert np.all(res["out"][r0:r0 + Hq] == 0.0) and np.all(res["lse"][r0:r0 + Hq] == -np.inf)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_multi_query_unified_max(kernel):
+    base = synth.Workload("mqu", B=1, Hq=16, Hkv=4, d=128, dtype="bf16", split=256, N=1, q_len=4,
+                          stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, (3000, 700)))
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi))
+    must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may])
+    assert res["count"] == int(got.sum()) and 0 < got.sum() < got.size
+    ft.check_exact(res, inp, what=f"q_len=4 unified {kernel}")
+
+
+def test_multi_query_rows_match_single_query_runs_bitwise():
+    """Each query row equals a one-token decode of the same q row at its causal
+    length, run through the library: same split boundaries and, with q_len * G
+    and G both at most 4, the same two-wave launch shape (rows of a matrix
+    tile are computed independently), so the same bits."""
+    base = synth.Workload("mqs", B=1, Hq=16, Hkv=8, d=128, dtype="bf16", split=256, N=1, q_len=2)
+    inp = synth.make_inputs(synth.with_lens(base, (2000, 513)))
+    res = Run(inp).run(kernel="mfma")
+    w = inp.w
+    for b in range(w.B):
+        for i in range(w.q_len):
+            n = int(inp.seq_lens[b]) - w.q_len + i + 1
+            w1 = dataclasses.replace(w, B=1, q_len=1, N=w.N, fixed_lens=(n,), name="mqs1")
+            inp1 = synth.Inputs(w1, inp.q[b, i][None].copy(), inp.k[b:b + 1].copy(), inp.v[b:b + 1].copy(),
+                                np.array([n], np.int32))
+            r1 = Run(inp1).run(kernel="mfma")
+            r = slice((b * w.q_len + i) * w.Hq, (b * w.q_len + i + 1) * w.Hq)
+            assert np.array_equal(res["lse"][r], r1["lse"]), (b, i)
+            assert np.array_equal(res["out"][r], r1["out"]), (b, i)
+
+
+def test_verify_4_tokens_long_context_gqa_full():
+    w = synth.WORKLOADS["long_gqa_32k_verify4"]
+    say("[long_gqa_32k_verify4] generating")
+    inp = synth.make_inputs(w)
+    res = Run(inp).run()
+    e1, e2 = ft.check_exact(res, inp, what="long_gqa_32k_verify4")
+    ft.check_partials(res, inp, w.split, what="long_gqa_32k_verify4")
+    say(f"[long_gqa_32k_verify4] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
