@@ -2,9 +2,12 @@
 // (f16 / bf16 caches).
 //
 // Work decomposition (as in the VALU kernel): one workgroup per (request b,
-// KV head, split s) covering all G query heads of that KV head, so K and V are
+// KV head, split s) covering all query rows of that KV head -- its G query
+// heads times the request's q_len query tokens, at most 16 -- so K and V are
 // read from HBM once per group (handbook page "FlashAttention and inference
 // kernels", exercise 3).  Each wave walks 16-token blocks of the split.
+// 8-bit (E4M3) caches are widened exactly to the 16-bit operand type in
+// registers before the LDS tiles; everything after the tiles is shared.
 //
 // Per block:
 //   loads: K and V rows with 16-byte non-temporal loads, 16 lanes per 256-byte
@@ -13,7 +16,7 @@
 //      2 * (row & 7), so the two operand reads below are bank-conflict-free.
 //   S^T[token][head] = K q^T: D / 32 v_mfma_f32_16x16x32; A = the K tile
 //      (lane l: token l % 16, dims 8 * (l / 16) .. + 8 of each 32-dim step),
-//      B = q of the group (heads >= G zero).  Result lane l: head l % 16,
+//      B = q of the group's query rows (rows >= R zero).  Result lane l: row l % 16,
 //      tokens 4 * (l / 16) .. + 3 of the block.
 //   softmax in that layout: SYNC keeps a running per-head maximum across the
 //      wave's blocks (page "FlashAttention and inference kernels", section
@@ -589,8 +592,8 @@ Shape launch_shape(const PartialParams &p) {
     // 8-bit caches: a block is half the bytes for the same compute, so a wave
     // without prefetch waits out a memory round trip per 4 KiB; always overlap
     const bool f8 = p.dtype == FP8;
-    // groups of more than four heads: one wave per workgroup (B=4, N=128k,
-    // G=8 and B=64 paged batches measured no slower than with two)
+    // more than four query rows per KV head: one wave per workgroup (B=4,
+    // N=128k, G=8 and B=64 paged batches measured no slower than with two)
     if (p.R > 4) return Shape{1, f8};
     // fewer than four workgroups per CU: each SIMD runs one or two waves and a
     // wave's own load-then-compute chain sets the pace, so overlap the two
