@@ -578,3 +578,25 @@ def test_verify_4_tokens_long_context_gqa_full():
     e1, e2 = ft.check_exact(res, inp, what="long_gqa_32k_verify4")
     ft.check_partials(res, inp, w.split, what="long_gqa_32k_verify4")
     say(f"[long_gqa_32k_verify4] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+
+
+# ----------------------------------------------------------------------------
+# the split the heuristic picks is a valid launch for every kernel
+# ----------------------------------------------------------------------------
+HEURISTIC_CASES = [  # (B, Hq, Hkv, lens, page)
+    ((1, 32, 8, (32768,), 0)), ((1, 8, 8, (700,), 0)), ((4, 32, 32, (4096, 100, 3000, 1), 0)),
+    ((2, 64, 8, (9000, 2049), 16)), ((3, 16, 16, (77, 300, 129), 16)),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,page", HEURISTIC_CASES)
+def test_heuristic_split_runs_and_matches_the_oracle(B, Hq, Hkv, lens, page):
+    import decode_attention_attn_amd as fd
+    split, S = fd.fd_split_heuristic(B, Hq, Hkv, max(lens), page, 256)
+    base = synth.Workload("heur", B=B, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", split=split, N=1, page_size=page)
+    inp = synth.make_inputs(synth.with_lens(base, lens))
+    res = Run(inp).run()
+    say(f"[heuristic] split={split} S={S} (cache S_max {res['part_m'].shape[1]})")
+    rows = ft.sample_rows(inp.w, 128, seed=9)
+    ft.check_exact(res, inp, rows=rows, what=f"heuristic split {split}")
+    ft.check_partials(res, inp, split, rows=rows, what=f"heuristic split {split}")
