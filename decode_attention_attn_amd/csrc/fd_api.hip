@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "fd_decode_attn.h"
 #include "fd_internal.h"
 
@@ -47,17 +49,20 @@ fd_status validate_desc(const fd_decode_desc *d) {
     return FD_OK;
 }
 
-// Compute units of the current device, read once per device.
+// Compute units of the current device, read once per device (host threads
+// may race to fill an entry; they store the same value).
 int32_t device_cus() {
-    static int32_t cached[64] = {0};
+    static std::atomic<int32_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-        cached[dev] = n;
+    int32_t n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+        n = v;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 fd::PartialParams base_params(const fd_decode_desc *d) {
