@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--lo", type=float, default=-20.0)
     ap.add_argument("--hi", type=float, default=20.0)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--split", type=int, default=0,
+                    help="split size override (default: the workload's; a sweep knob, not the headline)")
     ap.add_argument("--warm", action="store_true", help="one KV copy (cache-resident for small caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -321,6 +323,9 @@ def main():
 
     import synth
     w = synth.WORKLOADS[args.workload]
+    if args.split:
+        import dataclasses
+        w = dataclasses.replace(w, split=args.split)
     log(f"[bench] generating {w.name}")
     inp = synth.make_inputs(w, poison_tail=False)
     alg = algorithmic_bytes(inp)

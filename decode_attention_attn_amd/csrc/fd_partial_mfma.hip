@@ -131,7 +131,7 @@ struct MSmem {
     static constexpr int GQ = (GMAX + 3) / 4;      // head quads
     struct Fin {
         float4 acc[WAVES][D][GQ];                 // each wave's P x V rows: [dim][head quad]
-        float l[WAVES][4][GMAX];                  // every MFMA lane group's partial sums
+        float l[WAVES][GMAX];                     // each wave's l per query row
         float m[WAVES][GMAX];
     };
     union {
@@ -459,9 +459,13 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
         for (int i = 0; i < C::SL; ++i)
             sm.fin.acc[wave][16 * i + mrow][mq] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
     }
-    if (mrow < GMAX) {
-        sm.fin.l[wave][mq][mrow] = st.l;
-        if (mq == 0) sm.fin.m[wave][mrow] = st.m;
+    // the four lane groups hold l over different tokens of a row: sum them in
+    // registers, (g0 + g1) + (g2 + g3) in every lane
+    float lsum = st.l + __shfl_xor(st.l, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (mrow < GMAX && mq == 0) {
+        sm.fin.l[wave][mrow] = lsum;
+        sm.fin.m[wave][mrow] = st.m;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < GQ * D; idx += C::THREADS) {
@@ -487,8 +491,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
                 f[r] = 0.f;
                 if (g < GMAX) {
                     f[r] = rescale(sm.fin.m[w][g], M[r]);
-                    const float lw = (sm.fin.l[w][0][g] + sm.fin.l[w][1][g]) + (sm.fin.l[w][2][g] + sm.fin.l[w][3][g]);
-                    L[r] = fmaf(lw, f[r], L[r]);
+                    L[r] = fmaf(sm.fin.l[w][g], f[r], L[r]);
                 }
             }
             A.x = fmaf(aw.x, f[0], A.x);
