@@ -44,7 +44,7 @@ PARTIAL_KERNEL = "partial"        # substring of the split-partial kernels' name
 COPY_BYTES = 256 * 2 ** 20        # calibration copy: reads and writes this many bytes
 COMBINE_KERNEL = "combine_kernel"
 KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/fd_partial_valu.hip",
-                  "decode_attention_attn_amd/csrc/fd_partial_mfma.hip",
+                  "decode_attention_attn_amd/csrc/fd_partial_mfma.h",
                   "decode_attention_attn_amd/csrc/fd_device.h",
                   "decode_attention_attn_amd/csrc/fd_combine.hip"]
 
@@ -71,8 +71,8 @@ def algorithmic_bytes(inp):
     eb = synth.ELEM_BYTES[w.dtype]
     qb = synth.ELEM_BYTES[w.q_dtype]       # q and out (out has q's type)
     kv = inp.kv_bytes
-    q = w.B * w.Hq * w.d * qb
-    out = w.B * w.Hq * w.d * qb
+    q = w.B * w.q_len * w.Hq * w.d * qb
+    out = w.B * w.q_len * w.Hq * w.d * qb
     table = 0
     if w.page_size:
         table = int(((inp.seq_lens.astype(np.int64) + w.page_size - 1) // w.page_size).sum()) * 4
@@ -116,11 +116,11 @@ def run_gpu(args, inp, wl):
     mode = args.mode
     f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
     desc = fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, split_size=w.split, max_seq_len=w.N, mode=mode,
-                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel, **f8)
+                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel, q_len=w.q_len, **f8)
     S = desc.max_splits
-    out = torch.empty((w.B, w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device=dev)
-    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
-    flags = torch.zeros((w.B, w.Hq, S), dtype=torch.uint8, device=dev) if mode == "unified" else None
+    out = torch.empty((w.B, w.q_len * w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device=dev)
+    lse = torch.empty((w.B, w.q_len * w.Hq), dtype=torch.float32, device=dev)
+    flags = torch.zeros((w.B, w.q_len * w.Hq, S), dtype=torch.uint8, device=dev) if mode == "unified" else None
     count = torch.zeros(1, dtype=torch.int32, device=dev) if mode == "unified" else None
     L = fd.lib()
     stream = torch.cuda.current_stream()
@@ -130,7 +130,7 @@ def run_gpu(args, inp, wl):
 
     if w.page_size:
         ws = fd.alloc_workspace(desc, dev)
-        n = w.B * w.Hq * S
+        n = w.B * w.q_len * w.Hq * S
         o_b = (n * w.d * 4 + 255) // 256 * 256
         m_b = (n * 4 + 255) // 256 * 256
         fw = ws.view(torch.float32)
@@ -215,8 +215,9 @@ def fallback_stats(inp, flags, args):
     that hold tokens; each flagged one was recomputed with the synchronized softmax."""
     w = inp.w
     S = flags.shape[-1]
-    per_req = np.minimum(-(-inp.seq_lens.astype(np.int64) // w.split), S)
-    valid = int(per_req.sum()) * w.Hq
+    lens = inp.seq_lens.astype(np.int64)[:, None]
+    causal = np.clip(lens - w.q_len + np.arange(w.q_len)[None, :] + 1, 0, lens)   # tokens each query row sees
+    valid = int(np.minimum(-(-causal // w.split), S).sum()) * w.Hq
     n = int(flags.astype(np.int64).sum())
     return {"flagged_splits": n, "splits_with_tokens": valid, "rate": n / max(valid, 1),
             "phi": args.phi, "lo": args.lo, "hi": args.hi}
@@ -234,13 +235,35 @@ def parity_spot_check(inp, res, rows):
     return dict(rows=int(len(rows)), max_abs_err_out=float(e.max()), max_abs_err_lse=float(el.max()), ok=ok)
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, alg, seconds):
     """The fp64 oracle, as it is, on the host cores: whole decode steps of the
-    same workload repeated until about `seconds` of work have run."""
+    same workload repeated until about `seconds` of work have run (all host
+    threads), then a shorter single-thread sample of the same rows."""
     import oracle
     p = oracle.problem_of(inp)
     threads = oracle.default_threads()
-    R = inp.w.B * inp.w.Hq
+    R = inp.w.B * inp.w.q_len * inp.w.Hq         # query rows of one step
+
+    def timed_rows(rows, nthreads, budget):
+        reps, t = 0, time.perf_counter()
+        while True:
+            oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table,
+                             rows=rows, threads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= budget or reps >= 1000:
+                return reps, el
+
     # bounded sample: all rows when one step fits the budget, else a prefix of rows
     t = time.perf_counter()
     rows = np.arange(min(R, 8), dtype=np.int32)
@@ -249,20 +272,15 @@ def cpu_baseline(inp, alg, seconds):
     per_row = (time.perf_counter() - t) / len(rows)
     n_rows = int(min(R, max(1, seconds / max(per_row, 1e-9))))
     rows = np.arange(n_rows, dtype=np.int32)
-    reps = 0
-    t = time.perf_counter()
-    while True:
-        oracle.attention(p, inp.q, inp.k, inp.v, seq_lens=inp.seq_lens, block_table=inp.block_table, rows=rows,
-                         threads=threads)
-        reps += 1
-        el = time.perf_counter() - t
-        if el >= seconds or reps >= 1000:
-            break
+    reps, el = timed_rows(rows, threads, seconds)
     step_s = el / reps * (R / n_rows)          # scaled to a whole step
+    n1 = max(1, min(n_rows, threads))          # single thread: a few of the same rows
+    reps1, el1 = timed_rows(rows[:n1], 1, seconds / 4)
+    step1_s = el1 / reps1 * (R / n1)
     return {"value": alg["step"] / step_s / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
-            "us_per_step": step_s * 1e6,
-            "sample": f"{reps} x {n_rows}/{R} (request, query head) rows of the same workload, "
-                      f"{el:.1f} s of fp64 oracle work, scaled to one step"}
+            "us_per_step": step_s * 1e6, "single_thread_us_per_step": step1_s * 1e6, "cpu": _cpu_model(),
+            "sample": f"{reps} x {n_rows}/{R} query rows of the same workload, {el:.1f} s of fp64 oracle work "
+                      f"on {threads} threads, scaled to one step; single thread: {reps1} x {n1} rows, {el1:.1f} s"}
 
 
 def run_settings(args):
@@ -332,7 +350,7 @@ def main():
     g = run_gpu(args, inp, w)
     part_s = float(np.mean(g["part_us"])) * 1e-6
     step_s = g["step_ms"] * 1e-3
-    parity = parity_spot_check(inp, g["res"], np.arange(0, w.B * w.Hq, max(1, (w.B * w.Hq) // 32)))
+    parity = parity_spot_check(inp, g["res"], np.arange(0, w.B * w.q_len * w.Hq, max(1, (w.B * w.q_len * w.Hq) // 32)))
     log(f"[bench] step {g['step_ms'] * 1e3:.2f} us, partial {np.mean(g['part_us']):.2f} us, "
         f"combine {np.mean(g['comb_us']):.2f} us (back-to-back averages); parity {parity}")
     kname = "fd_decode_attn_paged" if w.page_size else PARTIAL_KERNEL
@@ -353,7 +371,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N, "q_len": w.q_len,
                    "kv_dtype": w.dtype, "split": w.split, "num_splits": g["S"], "page_size": w.page_size,
                    "softmax": args.mode, "kernel": args.kernel, "kv_copies": g["copies"],
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},

@@ -62,6 +62,11 @@ struct CombineParams {
 // launch status.
 hipError_t launch_partial_valu(const PartialParams &p, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialParams &p, hipStream_t stream);
+// one per instantiation type (operand type, and whether the cache is E4M3)
+hipError_t launch_partial_mfma_f16(const PartialParams &p, hipStream_t stream);
+hipError_t launch_partial_mfma_bf16(const PartialParams &p, hipStream_t stream);
+hipError_t launch_partial_mfma_f8f16(const PartialParams &p, hipStream_t stream);
+hipError_t launch_partial_mfma_f8bf16(const PartialParams &p, hipStream_t stream);
 bool mfma_supports(const PartialParams &p);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 

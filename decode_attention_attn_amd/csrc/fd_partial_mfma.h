@@ -1,0 +1,662 @@
+// fd_partial_mfma.h -- split-partial kernel on the gfx950 matrix cores
+// (f16 / bf16 / E4M3 caches).  Included by one translation unit per
+// instantiation type (fd_partial_mfma_<type>.hip), which keeps each unit's
+// compile short; fd_partial_mfma.hip holds the dispatch.
+//
+// Work decomposition (as in the VALU kernel): one workgroup per (request b,
+// KV head, split s) covering all query rows of that KV head -- its G query
+// heads times the request's q_len query tokens, at most 16 -- so K and V are
+// read from HBM once per group (handbook page "FlashAttention and inference
+// kernels", exercise 3).  Each wave walks 16-token blocks of the split.
+// 8-bit (E4M3) caches are widened exactly to the 16-bit operand type in
+// registers before the LDS tiles; everything after the tiles is shared.
+//
+// Per block:
+//   loads: K and V rows with 16-byte non-temporal loads, 16 lanes per 256-byte
+//      row (coalesced), written to wave-private LDS tiles.  The K tile's
+//      16-byte chunks are XOR-swizzled by (row & 15), the V tile's by
+//      2 * (row & 7), so the two operand reads below are bank-conflict-free.
+//   S^T[token][head] = K q^T: D / 32 v_mfma_f32_16x16x32; A = the K tile
+//      (lane l: token l % 16, dims 8 * (l / 16) .. + 8 of each 32-dim step),
+//      B = q of the group's query rows (rows >= R zero).  Result lane l: row l % 16,
+//      tokens 4 * (l / 16) .. + 3 of the block.
+//   softmax in that layout: SYNC keeps a running per-head maximum across the
+//      wave's blocks (page "FlashAttention and inference kernels", section
+//      "FlashAttention: tiling plus online softmax"); UNIFIED uses the fixed
+//      constant phi and checks every score against [lo, hi] (page
+//      "FlashDecoding++: Faster Large Language Model Inference on GPUs",
+//      Eq. 3 / Eq. 4 and "The Overflow Fallback: Recomputation").
+//   O[head][dim] += P V: D / 16 slices of v_mfma_f32_16x16x16.  The result
+//      layout of S^T is the A-operand layout of P (head l % 16, tokens
+//      4 * (l / 16) + e), so the probabilities stay in registers; they enter
+//      as a 16-bit high part plus the 16-bit rounding of the fp32 residual
+//      (two MFMAs), which keeps the weights to about 14 bits or better.
+//      B (lane j of lane group q: V[token 4q + k][dim j] of the slice) comes
+//      from the V tile with ds_read_b64_tr_b16, whose result is lane j,
+//      element k = element j % 4 of the 8-byte row addressed by lane 4k + j / 4
+//      of the group.  O lands with heads on rows: 4 registers per slice,
+//      independent of G, and no cross-lane reduction at the end.
+// The wave states are merged across waves by the max-rescale rule and
+// written as one split partial.
+#pragma once
+
+#include "fd_device.h"
+
+namespace fd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4 &a, const uint4 &b, f32x4 c) {
+    if constexpr (DT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                     0, 0, 0);
+}
+
+// O += P V for one 16-dim slice: A = 4 probabilities, B = 4 values (16-bit each)
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x16(const s16x4 &a, const s16x4 &b, f32x4 c) {
+    if constexpr (DT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                    0, 0, 0);
+}
+
+// Four fp32 probabilities -> 16-bit high parts and 16-bit parts of the exact
+// fp32 residuals, packed as MFMA operands.  bf16: the high part is the top
+// 16 bits (truncation); f16: round toward zero.  Either way hi + lo carries
+// the weight to a relative error below 2^-14.
+template <int DT>
+__device__ __forceinline__ void split_probs(const float (&pr)[4], s16x4 &hi, s16x4 &lo) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float a = pr[2 * i], b = pr[2 * i + 1];
+        if constexpr (DT == BF16) {
+            const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+            const float ra = a - __uint_as_float(ua & 0xffff0000u);
+            const float rb = b - __uint_as_float(ub & 0xffff0000u);
+            h[i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);      // [ua.hi16 | ub.hi16 << 16]
+            l[i] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+        } else {
+            const auto hh = __builtin_amdgcn_cvt_pkrtz(a, b);
+            const float ra = a - (float)hh[0], rb = b - (float)hh[1];
+            const auto ll = __builtin_amdgcn_cvt_pkrtz(ra, rb);
+            h[i] = __builtin_bit_cast(uint32_t, hh);
+            l[i] = __builtin_bit_cast(uint32_t, ll);
+        }
+    }
+    hi = __builtin_bit_cast(s16x4, make_uint2(h[0], h[1]));
+    lo = __builtin_bit_cast(s16x4, make_uint2(l[0], l[1]));
+}
+
+constexpr int kBlk = 16;   // tokens per MFMA block
+
+// Instantiation type T: the 16-bit operand type of the matrix instructions
+// (F16 or BF16, also the type of q), plus 16 when the cache holds 8-bit E4M3
+// values that are widened to it in registers (exactly: an E4M3 value has four
+// significant bits and its exponent range fits both 16-bit types).
+constexpr int kF8 = 16;
+__host__ __device__ constexpr int op_of(int T) { return T & 15; }
+__host__ __device__ constexpr bool f8_of(int T) { return T >= kF8; }
+
+// How a block's cache rows are loaded: 16 bytes per lane, LPR lanes per row.
+template <int T, int D>
+struct KLoad {
+    static constexpr int EB = f8_of(T) ? 1 : 2;     // bytes per cache element
+    static constexpr int LPR = D * EB / 16;         // lanes per row
+    static constexpr int RPI = 64 / LPR;            // rows per load instruction
+    static constexpr int LI = kBlk / RPI;           // load instructions per block (K, and again V)
+};
+
+template <int D, int GMAX, int WAVES>
+struct MCfg {
+    static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension (QK)
+    static constexpr int SL = D / 16;                 // 16-dim output slices (PV)
+    static constexpr int LPR = D / 8;                 // lanes per row in the natural layout
+    static constexpr int RPI = 64 / LPR;              // rows per load instruction
+    static constexpr int LI = kBlk / RPI;             // load instructions per block
+    static constexpr int ROWB = D * 2;                // bytes per cache row
+    static constexpr int THREADS = 64 * WAVES;
+};
+
+template <int D, int GMAX, int WAVES>
+struct MSmem {
+    using C = MCfg<D, GMAX, WAVES>;
+    static constexpr int GQ = (GMAX + 3) / 4;      // head quads
+    struct Fin {
+        float4 acc[WAVES][D][GQ];                 // each wave's P x V rows: [dim][head quad]
+        float l[WAVES][GMAX];                     // each wave's l per query row
+        float m[WAVES][GMAX];
+    };
+    union {
+        uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tiles ...
+        Fin fin;                                  // ... reused by the epilogue once every wave is done
+    };
+    uint4 v[WAVES][kBlk * C::ROWB / 16];          // wave-private V tiles
+    float corr[WAVES][16];                        // running-max rescale factors per head row
+    uint32_t bad[WAVES];
+};
+
+template <int D, int GMAX>
+struct MState {
+    float m, l;             // head l % 16 (S^T layout)
+    bool bad;
+    f32x4 o[D / 16];        // O[head 4 * (l / 16) + r][16 * slice + l % 16]
+    __device__ void init(float m0) {
+        m = m0;
+        l = 0.f;
+        bad = false;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+// Rows of one 16-token block: where they live and whether their page exists.
+struct BlockRows {
+    int tb;          // first token of the block
+    size_t row0;     // element offset of (token tb, kvh, dim 0); rows step by Hkv * d
+    bool page_ok;
+};
+
+// The split's block-table entries, one per lane (pages t0 / page .. + 63),
+// read once per workgroup; blocks beyond them read the table directly.
+struct PageCache {
+    int base;        // first page index held
+    int entry;       // this lane's entry: page base + lane
+};
+
+template <bool PAGED>
+__device__ __forceinline__ PageCache load_pages(const PartialParams &p, int b, int t0, int t1) {
+    PageCache pc{0, -1};
+    if constexpr (PAGED) {
+        const int lane = threadIdx.x & 63;
+        pc.base = t0 / p.page_size;
+        const int last = (t1 - 1) / p.page_size;          // t1 > t0 here
+        if (pc.base + lane <= last) pc.entry = p.block_table[(size_t)b * p.max_blocks + pc.base + lane];
+    }
+    return pc;
+}
+
+template <int D, bool PAGED>
+__device__ __forceinline__ BlockRows block_rows(const PartialParams &p, const PageCache &pc, int b, int kvh, int tb,
+                                                int t1) {
+    BlockRows r;
+    r.tb = tb;
+    r.page_ok = true;
+    const size_t head_off = (size_t)kvh * D;
+    if (tb >= t1) {                                       // past the split: every row reads the safe row
+        r.page_ok = false;
+        r.row0 = head_off;
+        return r;
+    }
+    if constexpr (PAGED) {
+        const int pg = tb / p.page_size;                  // wave-uniform
+        const int phys = pg - pc.base < 64 ? __builtin_amdgcn_readlane(pc.entry, pg - pc.base)
+                                           : p.block_table[(size_t)b * p.max_blocks + pg];
+        r.page_ok = phys >= 0 && phys < p.num_pages;
+        r.row0 = (((size_t)(r.page_ok ? phys : 0) * p.page_size + tb % p.page_size) * p.Hkv) * D + head_off;
+    } else {
+        r.row0 = (((size_t)b * p.kv_capacity + tb) * p.Hkv) * D + head_off;
+    }
+    return r;
+}
+
+// Block loads go through buffer resources: the wave-uniform base is the
+// block's first row, each lane's byte offset within a block is the same for
+// every block (computed once), and rows past the block's valid range lie
+// beyond num_records, so the hardware returns zeros for them without a memory
+// access.  Word 3 of a raw buffer resource on this GPU family: 32-bit data
+// format, no swizzle, no stride.
+constexpr int32_t kBufferWord3 = 0x00020000;
+constexpr int kLoadNT = 2;                            // cache policy: non-temporal (streamed once)
+
+template <int LI>
+struct LaneOffsets {
+    uint32_t k[LI], v[LI];
+};
+
+template <int T, int D>
+__device__ __forceinline__ LaneOffsets<KLoad<T, D>::LI> lane_offsets(const PartialParams &p) {
+    using L = KLoad<T, D>;
+    const int lane = threadIdx.x & 63;
+    const int rg = lane / L::LPR, ch = lane % L::LPR;
+    const uint32_t rbytes = (uint32_t)p.Hkv * D * L::EB;   // bytes between consecutive tokens of a head
+    LaneOffsets<L::LI> o;
+#pragma unroll
+    for (int i = 0; i < L::LI; ++i) {
+        const int r = i * L::RPI + rg;
+        // 16-bit K chunks arrive XOR-swizzled by row; 8-bit rows are swizzled
+        // when widened into the tile
+        o.k[i] = r * rbytes + 16 * (f8_of(T) ? ch : (ch ^ (r & (L::LPR - 1))));
+        o.v[i] = r * rbytes + 16 * ch;
+    }
+    return o;
+}
+
+// K and V of a block, 16 bytes per lane each.
+template <int T, int D>
+__device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1,
+                                           const LaneOffsets<KLoad<T, D>::LI> &off,
+                                           uint4 (&kr)[KLoad<T, D>::LI], uint4 (&vr)[KLoad<T, D>::LI]) {
+    using C = KLoad<T, D>;
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const int valid = br.page_ok ? max(0, min(kBlk, t1 - br.tb)) : 0;   // wave-uniform
+    const int32_t bytes = valid * p.Hkv * D * C::EB;
+    const char *kb = static_cast<const char *>(p.k) + br.row0 * C::EB;
+    const char *vb = static_cast<const char *>(p.v) + br.row0 * C::EB;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), 0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, bytes, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < C::LI; ++i) {
+        const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[i], 0, kLoadNT);
+        const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rv, off.v[i], 0, kLoadNT);
+        kr[i] = make_uint4(a.x, a.y, a.z, a.w);
+        vr[i] = make_uint4(c.x, c.y, c.z, c.w);
+    }
+}
+
+// 16 E4M3 values -> 16 values of the operand type, as two 16-byte chunks.
+// gfx950's v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1 converts two values
+// per instruction, exactly for all 256 codes (checked on the hardware): an
+// E4M3 value has four significant bits and its exponents fit both types.
+template <int OP>
+__device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (OP == BF16) {
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+        } else {
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+        }
+    }
+    lo = make_uint4(o[0], o[1], o[2], o[3]);
+    hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// lim: this lane's query row (lane % 16) sees tokens < lim of the split
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int lim,
+                                              const uint4 (&kr)[KLoad<T, D>::LI],
+                                              const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
+                                              MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+    using C = MCfg<D, GMAX, WAVES>;
+    using L = KLoad<T, D>;
+    constexpr int DT = op_of(T);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = lane / L::LPR, ch = lane % L::LPR;
+    const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
+    char *ktile = reinterpret_cast<char *>(sm.k[wave]);
+    char *vtile = reinterpret_cast<char *>(sm.v[wave]);
+    // tiles: 16-byte chunk c of row r lives at slot c ^ (r & (LPR-1)) (K) and
+    // c ^ (2 * (r & (LPR/2 - 1))) (V), LPR = D / 8 chunks per row
+#pragma unroll
+    for (int i = 0; i < L::LI; ++i) {
+        const int r = i * L::RPI + rg;
+        if constexpr (f8_of(T)) {   // this lane's 16 values are chunks 2 ch and 2 ch + 1
+            uint4 k0, k1, v0, v1;
+            widen_f8<DT>(kr[i], k0, k1);
+            widen_f8<DT>(vr[i], v0, v1);
+            const int c = 2 * ch, ks = r & (C::LPR - 1), vs = 2 * (r & (C::LPR / 2 - 1));
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c ^ ks)) = k0;
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * ((c + 1) ^ ks)) = k1;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (c ^ vs)) = v0;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * ((c + 1) ^ vs)) = v1;
+        } else {                    // K chunks arrive pre-swizzled
+            *reinterpret_cast<uint4 *>(ktile + i * L::RPI * C::ROWB + lane * 16) = kr[i];
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
+        }
+    }
+
+    // ---- S^T = K q^T on the matrix cores
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const int slot = (4 * ks + mq) ^ (mrow & (C::LPR - 1));
+        const uint4 a = *reinterpret_cast<const uint4 *>(ktile + mrow * C::ROWB + slot * 16);
+        acc = mfma16x16x32<DT>(a, qop[ks], acc);
+    }
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = br.page_ok && br.tb + 4 * mq + r < lim;
+        s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
+    }
+
+    // ---- softmax for head mrow over these 16 tokens
+    float pr[4];
+    if constexpr (UNIFIED) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            st.bad = st.bad || (s[r] != -INFINITY && (s[r] < p.lo2 || s[r] > p.hi2));
+            pr[r] = exp2_fast(s[r] - p.phi2);
+            st.l += pr[r];
+        }
+    } else {
+        float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(st.m, mt);
+        const float corr = rescale(st.m, mn);
+        const bool moved = mn != st.m;
+        st.m = mn;
+        st.l *= corr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = mn == -INFINITY ? 0.f : exp2_fast(s[r] - mn);
+            st.l += pr[r];
+        }
+        // rescale the P x V accumulators (heads on rows 4 * (l / 16) + r)
+        if (__any(moved)) {
+            if (lane < 16) sm.corr[wave][lane] = corr;
+            const float4 cf = *reinterpret_cast<const float4 *>(&sm.corr[wave][4 * mq]);
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) {
+                st.o[i][0] *= cf.x;
+                st.o[i][1] *= cf.y;
+                st.o[i][2] *= cf.z;
+                st.o[i][3] *= cf.w;
+            }
+        }
+    }
+
+    // ---- O += P V on the matrix cores
+    s16x4 phi, plo;
+    split_probs<DT>(pr, phi, plo);
+    // this lane's 8-byte row of the transposing read: token 4 * mq + mrow / 4,
+    // dims 16 * slice + 4 * (mrow % 4) .. + 3
+    const int vrow = 4 * mq + (mrow >> 2);
+    const char *vrow_base = vtile + vrow * C::ROWB;
+    const int vsw = 2 * (vrow & (C::LPR / 2 - 1));
+#pragma unroll
+    for (int i = 0; i < C::SL; ++i) {
+        const int dim = 16 * i + 4 * (mrow & 3);
+        const int slot = (dim >> 3) ^ vsw;
+        const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
+        st.o[i] = mfma16x16x16<DT>(phi, bv, st.o[i]);
+        st.o[i] = mfma16x16x16<DT>(plo, bv, st.o[i]);
+    }
+}
+
+// One wave's share of the split: blocks wave, wave + WAVES, ...  With PF the
+// loads of the wave's next block are issued before the current block is
+// computed, so a wave keeps two blocks in flight.  Paged caches read the
+// split's block-table entries once (one per lane) and pick each block's page
+// from them with a lane read.
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, int lim, const uint4 (&qop)[D / 32],
+                           MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+    using L = KLoad<T, D>;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const auto off = lane_offsets<T, D>(p);
+    const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+    const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
+    if constexpr (PF) {
+        // ping-pong: block A computes while block B loads, then the roles swap
+        // (unrolled by two so no register copy has to wait on in-flight loads).
+        // The loop runs while a full A-B-A step remains and issues its loads
+        // unconditionally; the last one or two blocks are peeled off.  A load
+        // under a branch would make the compiler's wait at the join cover the
+        // prefetched block as well, and a load past the split would make the
+        // epilogue wait for a useless block.
+        const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
+        if (n == 0) return;
+        const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
+        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1), rb;
+        uint4 ka[L::LI], va[L::LI], kb2[L::LI], vb2[L::LI];
+        load_block<T, D>(p, ra, t1, off, ka, va);
+        int j = 0;
+        for (; j + 2 < n; j += 2) {
+            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+            load_block<T, D>(p, rb, t1, off, kb2, vb2);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
+            ra = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 2) * tstep, t1);
+            load_block<T, D>(p, ra, t1, off, ka, va);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
+        }
+        if (j + 2 == n) {
+            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+            load_block<T, D>(p, rb, t1, off, kb2, vb2);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
+        } else {
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
+        }
+    } else {
+        for (int blk = wave; blk < nblk; blk += WAVES) {
+            const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
+            uint4 kr[L::LI], vr[L::LI];
+            load_block<T, D>(p, br, t1, off, kr, vr);
+            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, kr, vr, qop, st, sm);
+        }
+    }
+}
+
+// Wave states -> LDS -> the split's partial for the heads in write_mask.  The
+// P x V rows are already per head (lane group q holds heads 4q .. 4q + 3 of
+// one dim per slice, one 16-byte LDS store each); after one barrier each
+// thread merges one dim of four heads over the waves by the max-rescale rule.
+template <int T, int D, int GMAX, int WAVES>
+__device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
+                             int s, uint32_t write_mask) {
+    using C = MCfg<D, GMAX, WAVES>;
+    constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mrow = lane & 15, mq = lane >> 4;
+    __syncthreads();   // the epilogue area overlays the K tiles of every wave
+    if (mq < GQ) {
+#pragma unroll
+        for (int i = 0; i < C::SL; ++i)
+            sm.fin.acc[wave][16 * i + mrow][mq] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
+    }
+    // the four lane groups hold l over different tokens of a row: sum them in
+    // registers, (g0 + g1) + (g2 + g3) in every lane
+    float lsum = st.l + __shfl_xor(st.l, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (mrow < GMAX && mq == 0) {
+        sm.fin.l[wave][mrow] = lsum;
+        sm.fin.m[wave][mrow] = st.m;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < GQ * D; idx += C::THREADS) {
+        const int gq = idx / D, dim = idx % D;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+        float L[4] = {0.f, 0.f, 0.f, 0.f}, M[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * gq + r;
+            M[r] = -INFINITY;
+            if (g < GMAX) {
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) M[r] = fmaxf(M[r], sm.fin.m[w][g]);
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float4 aw = sm.fin.acc[w][dim][gq];
+            float f[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int g = 4 * gq + r;
+                f[r] = 0.f;
+                if (g < GMAX) {
+                    f[r] = rescale(sm.fin.m[w][g], M[r]);
+                    L[r] = fmaf(sm.fin.l[w][g], f[r], L[r]);
+                }
+            }
+            A.x = fmaf(aw.x, f[0], A.x);
+            A.y = fmaf(aw.y, f[1], A.y);
+            A.z = fmaf(aw.z, f[2], A.z);
+            A.w = fmaf(aw.w, f[3], A.w);
+        }
+        const float a4[4] = {A.x, A.y, A.z, A.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * gq + r;
+            if (g >= p.R || !((write_mask >> g) & 1u)) continue;
+            const size_t slot = row_slot(p, b, kvh, g, s);
+            float o = L[r] > 0.f ? a4[r] / L[r] : 0.f;
+            if constexpr (f8_of(T)) o *= p.v_mult;   // a stored V unit stands for v_scale
+            p.part_o[slot * D + dim] = o;
+            if (dim == 0) {
+                p.part_m[slot] = (L[r] > 0.f && M[r] != -INFINITY) ? M[r] * kLn2 : -INFINITY;
+                p.part_l[slot] = L[r];
+            }
+        }
+    }
+}
+
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNI>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4)))
+partial_mfma_kernel(const PartialParams p) {
+    using C = MCfg<D, GMAX, WAVES>;
+    static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
+    __shared__ MSmem<D, GMAX, WAVES> sm;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
+    const int R = p.R;                               // query rows of this KV head
+    const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
+    const int t0 = s * p.split;
+    const int t1 = min(t0 + p.split, len);
+
+    if (t0 >= t1) {
+        if (threadIdx.x < R) {
+            const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
+            p.part_m[slot] = -INFINITY;
+            p.part_l[slot] = 0.f;
+            if (p.flags) p.flags[slot] = 0;
+        }
+        return;
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // B operand: q of query row (lane % 16), dims 8 * (lane / 16) of each step
+    uint4 qop[C::KS];
+    const int lim = row_limit(p, len, t1, lane & 15);
+    {
+        const int rho = lane & 15;
+        const char *qb = static_cast<const char *>(p.q);
+        const size_t qrow = rho < R ? query_row(p, b, kvh, rho) : 0;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            qop[ks] = make_uint4(0, 0, 0, 0);
+            if (rho < R) qop[ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
+        }
+    }
+
+    const uint32_t all = (1u << R) - 1u;
+    MState<D, GMAX> st;
+    uint32_t badmask = 0;
+    if constexpr (UNI) {
+        st.init(p.phi2);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        const uint64_t bal = __ballot(st.bad);
+        const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
+        if (lane == 0) sm.bad[wave] = mine;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
+        badmask &= all;
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all & ~badmask);
+        if (badmask) {   // synchronized recompute of the flagged heads
+            __syncthreads();
+            st.init(-INFINITY);
+            scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+            finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, badmask);
+        }
+        if (threadIdx.x == 0 && badmask && p.fallback_count)
+            atomicAdd(p.fallback_count, __builtin_popcount(badmask));
+    } else {
+        st.init(-INFINITY);
+        scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all);
+    }
+    if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
+}
+
+// Launch shape: waves per workgroup and whether a wave prefetches its next
+// block.  Chosen from measurements on MI355X.
+struct Shape {
+    int waves;
+    bool prefetch;
+};
+
+inline Shape launch_shape(const PartialParams &p) {
+    // 8-bit caches: a block is half the bytes for the same compute, so a wave
+    // without prefetch waits out a memory round trip per 4 KiB; always overlap
+    const bool f8 = p.dtype == FP8;
+    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B, per_cu4 = 4 * (int64_t)p.num_cus;
+    // more than four query rows per KV head in a grid of more than four
+    // workgroups per CU: one wave per workgroup (B=4, N=128k, G=8 and B=64
+    // paged batches measured no slower than with two); a grid the chip holds
+    // at once keeps two (32k GQA verifying 4 tokens, 16 rows)
+    if (p.R > 4 && wgs > per_cu4) return Shape{1, f8};
+    // fewer than four workgroups per CU: each SIMD runs one or two waves and a
+    // wave's own load-then-compute chain sets the pace, so overlap the two
+    // (Llama-2-7B-shaped MHA, 512 workgroups: 14.7 us against 15.5 us)
+    // (8-bit, 32k GQA: 2 waves 15.6 us, 4 waves 18.5 us -- 152 VGPRs leave
+    // room for 12 waves per CU, not the 16 that four 4-wave workgroups need)
+    return Shape{2, f8 || wgs < per_cu4};
+}
+
+template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED>
+hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
+    dim3 grid(p.max_splits, p.Hkv, p.B);
+    if (p.unified)
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, true>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, false>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    return hipGetLastError();
+}
+
+template <int T, int D, int GMAX, bool PAGED>
+hipError_t launch(const PartialParams &p, hipStream_t stream) {
+    const Shape sh = launch_shape(p);
+    if constexpr (GMAX > 4) {
+        if (sh.waves == 1) return launch_shaped<T, D, GMAX, 1, f8_of(T), PAGED>(p, stream);
+    }
+    if constexpr (f8_of(T)) {
+        return launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream);
+    } else {
+        return sh.prefetch ? launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream)
+                           : launch_shaped<T, D, GMAX, 2, false, PAGED>(p, stream);
+    }
+}
+
+template <int T, int D, int GMAX>
+hipError_t by_paged(const PartialParams &p, hipStream_t s) {
+    return p.page_size ? launch<T, D, GMAX, true>(p, s) : launch<T, D, GMAX, false>(p, s);
+}
+
+template <int T, int D>
+hipError_t by_group(const PartialParams &p, hipStream_t s) {
+    if (p.R <= 1) return by_paged<T, D, 1>(p, s);
+    if (p.R <= 2) return by_paged<T, D, 2>(p, s);
+    if (p.R <= 4) return by_paged<T, D, 4>(p, s);
+    if (p.R <= 8) return by_paged<T, D, 8>(p, s);
+    return by_paged<T, D, 16>(p, s);
+}
+
+template <int T>
+hipError_t by_dim(const PartialParams &p, hipStream_t s) {
+    return p.d == 64 ? by_group<T, 64>(p, s) : by_group<T, 128>(p, s);
+}
+
+}  // namespace
+}  // namespace fd
