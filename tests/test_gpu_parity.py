@@ -508,23 +508,25 @@ def test_fp8_long_context_gqa_full():
 # several causal query tokens per request (draft verification / a chunk of new
 # tokens already in the cache); q_len * G rows share one KV head
 # ----------------------------------------------------------------------------
-MQ_CASES = [  # (kernel, dtype, Hq, Hkv, q_len)
-    ("mfma", "bf16", 32, 8, 4), ("mfma", "bf16", 8, 8, 16), ("mfma", "f16", 16, 8, 8), ("mfma", "bf16", 24, 8, 5),
-    ("mfma", "fp8", 32, 8, 4), ("valu", "f32", 16, 8, 3), ("valu", "bf16", 32, 8, 4), ("valu", "fp8", 8, 8, 2),
+MQ_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d)
+    ("mfma", "bf16", 32, 8, 4, 128), ("mfma", "bf16", 8, 8, 16, 128), ("mfma", "f16", 16, 8, 8, 128),
+    ("mfma", "bf16", 24, 8, 5, 128), ("mfma", "fp8", 32, 8, 4, 128), ("mfma", "bf16", 16, 4, 3, 64),
+    ("valu", "f32", 16, 8, 3, 128), ("valu", "bf16", 32, 8, 4, 128), ("valu", "fp8", 8, 8, 2, 128),
+    ("valu", "f16", 8, 2, 4, 64),
 ]
 
 
 @pytest.mark.parametrize("page", [0, 16])
-@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len", MQ_CASES)
-def test_multi_query_causal(kernel, dtype, Hq, Hkv, q_len, page):
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", MQ_CASES)
+def test_multi_query_causal(kernel, dtype, Hq, Hkv, q_len, d, page):
     extra = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if dtype == "fp8" else {}
-    base = synth.Workload("mq", B=1, Hq=Hq, Hkv=Hkv, d=128, dtype=dtype, split=128, N=1, page_size=page,
+    base = synth.Workload("mq", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=128, N=1, page_size=page,
                           q_len=q_len, **extra)
     # lengths cover a split boundary inside the query window and a request
     # shorter than its query tokens
     inp = synth.make_inputs(synth.with_lens(base, (1000, 129, 130, 3, 2 * q_len)))
     res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel))
-    what = f"q_len={q_len} {kernel} {dtype} G={Hq // Hkv} page={page}"
+    what = f"q_len={q_len} {kernel} {dtype} d={d} G={Hq // Hkv} page={page}"
     ft.check_exact(res, inp, what=what)
     ft.check_partials(res, inp, 128, what=what)
     # query token 0 of the request of length 3 < q_len sees nothing when q_len > 3
