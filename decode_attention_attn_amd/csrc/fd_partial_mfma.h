@@ -243,6 +243,13 @@ __device__ __forceinline__ LaneOffsets<KLoad<T, D>::LI> lane_offsets(const Parti
     return o;
 }
 
+__device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
+    const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+}
+
 // K and V of a block, 16 bytes per lane each.
 template <int T, int D>
 __device__ __forceinline__ void load_block(const PartialParams &p, const BlockRows &br, int t1,
@@ -251,9 +258,11 @@ __device__ __forceinline__ void load_block(const PartialParams &p, const BlockRo
     using C = KLoad<T, D>;
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     const int valid = br.page_ok ? max(0, min(kBlk, t1 - br.tb)) : 0;   // wave-uniform
-    const int32_t bytes = valid * p.Hkv * D * C::EB;
-    const char *kb = static_cast<const char *>(p.k) + br.row0 * C::EB;
-    const char *vb = static_cast<const char *>(p.v) + br.row0 * C::EB;
+    // the resources are the same for every lane; say so, or the compiler wraps
+    // each load in a loop over distinct resource values
+    const int32_t bytes = __builtin_amdgcn_readfirstlane(valid * p.Hkv * D * C::EB);
+    const char *kb = uniform_ptr(static_cast<const char *>(p.k) + br.row0 * C::EB);
+    const char *vb = uniform_ptr(static_cast<const char *>(p.v) + br.row0 * C::EB);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), 0, bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, bytes, kBufferWord3);
 #pragma unroll
@@ -287,18 +296,16 @@ __device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi)
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// lim: this lane's query row (lane % 16) sees tokens < lim of the split
-template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int lim,
-                                              const uint4 (&kr)[KLoad<T, D>::LI],
-                                              const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
-                                              MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+// A block's K and V registers -> the wave's LDS tiles (the registers are
+// free again afterwards).
+template <int T, int D, int GMAX, int WAVES>
+__device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], const uint4 (&vr)[KLoad<T, D>::LI],
+                                            MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
     using L = KLoad<T, D>;
     constexpr int DT = op_of(T);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = lane / L::LPR, ch = lane % L::LPR;
-    const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
     char *ktile = reinterpret_cast<char *>(sm.k[wave]);
     char *vtile = reinterpret_cast<char *>(sm.v[wave]);
     // tiles: 16-byte chunk c of row r lives at slot c ^ (r & (LPR-1)) (K) and
@@ -320,6 +327,20 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
             *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
         }
     }
+}
+
+// One block from the wave's tiles into the running state.
+// lim: this lane's query row (lane % 16) sees tokens < lim of the split
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void compute_tiles(const PartialParams &p, const BlockRows &br, int lim,
+                                              const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
+                                              MSmem<D, GMAX, WAVES> &sm) {
+    using C = MCfg<D, GMAX, WAVES>;
+    constexpr int DT = op_of(T);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
+    const char *ktile = reinterpret_cast<const char *>(sm.k[wave]);
+    const char *vtile = reinterpret_cast<const char *>(sm.v[wave]);
 
     // ---- S^T = K q^T on the matrix cores
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -392,6 +413,15 @@ __device__ __forceinline__ void compute_block(const PartialParams &p, const Bloc
     }
 }
 
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int lim,
+                                              const uint4 (&kr)[KLoad<T, D>::LI],
+                                              const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
+                                              MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+    write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
+    compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
+}
+
 // One wave's share of the split: blocks wave, wave + WAVES, ...  With PF the
 // loads of the wave's next block are issued before the current block is
 // computed, so a wave keeps two blocks in flight.  Paged caches read the
@@ -437,11 +467,22 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
             compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
         }
     } else {
-        for (int blk = wave; blk < nblk; blk += WAVES) {
-            const BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + blk * kBlk, t1);
-            uint4 kr[L::LI], vr[L::LI];
-            load_block<T, D>(p, br, t1, off, kr, vr);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, kr, vr, qop, st, sm);
+        // one register set: once a block sits in the LDS tiles its registers
+        // take the next block's loads, which are then in flight during the
+        // block's matrix work.  The load after the last block is of an empty
+        // block (no rows in range), which reads no memory.
+        const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
+        if (n == 0) return;
+        const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
+        BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1);
+        uint4 kr[L::LI], vr[L::LI];
+        load_block<T, D>(p, br, t1, off, kr, vr);
+        for (int j = 0; j < n; ++j) {
+            write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
+            const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+            load_block<T, D>(p, bn, t1, off, kr, vr);
+            compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
+            br = bn;
         }
     }
 }
