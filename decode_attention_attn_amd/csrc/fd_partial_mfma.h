@@ -413,21 +413,10 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
     }
 }
 
-template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void compute_block(const PartialParams &p, const BlockRows &br, int lim,
-                                              const uint4 (&kr)[KLoad<T, D>::LI],
-                                              const uint4 (&vr)[KLoad<T, D>::LI], const uint4 (&qop)[D / 32],
-                                              MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
-    write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
-    compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
-}
-
-// One wave's share of the split: blocks wave, wave + WAVES, ...  With PF the
-// loads of the wave's next block are issued before the current block is
-// computed, so a wave keeps two blocks in flight.  Paged caches read the
-// split's block-table entries once (one per lane) and pick each block's page
-// from them with a lane read.
-template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNIFIED>
+// One wave's share of the split: blocks wave, wave + WAVES, ...  Paged caches
+// read the split's block-table entries once (one per lane) and pick each
+// block's page from them with a lane read.
+template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNIFIED>
 __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, int lim, const uint4 (&qop)[D / 32],
                            MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
     using L = KLoad<T, D>;
@@ -435,55 +424,22 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     const auto off = lane_offsets<T, D>(p);
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
     const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
-    if constexpr (PF) {
-        // ping-pong: block A computes while block B loads, then the roles swap
-        // (unrolled by two so no register copy has to wait on in-flight loads).
-        // The loop runs while a full A-B-A step remains and issues its loads
-        // unconditionally; the last one or two blocks are peeled off.  A load
-        // under a branch would make the compiler's wait at the join cover the
-        // prefetched block as well, and a load past the split would make the
-        // epilogue wait for a useless block.
-        const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
-        if (n == 0) return;
-        const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
-        BlockRows ra = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1), rb;
-        uint4 ka[L::LI], va[L::LI], kb2[L::LI], vb2[L::LI];
-        load_block<T, D>(p, ra, t1, off, ka, va);
-        int j = 0;
-        for (; j + 2 < n; j += 2) {
-            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
-            load_block<T, D>(p, rb, t1, off, kb2, vb2);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
-            ra = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 2) * tstep, t1);
-            load_block<T, D>(p, ra, t1, off, ka, va);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
-        }
-        if (j + 2 == n) {
-            rb = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
-            load_block<T, D>(p, rb, t1, off, kb2, vb2);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, rb, lim, kb2, vb2, qop, st, sm);
-        } else {
-            compute_block<T, D, GMAX, WAVES, UNIFIED>(p, ra, lim, ka, va, qop, st, sm);
-        }
-    } else {
-        // one register set: once a block sits in the LDS tiles its registers
-        // take the next block's loads, which are then in flight during the
-        // block's matrix work.  The load after the last block is of an empty
-        // block (no rows in range), which reads no memory.
-        const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
-        if (n == 0) return;
-        const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
-        BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1);
-        uint4 kr[L::LI], vr[L::LI];
-        load_block<T, D>(p, br, t1, off, kr, vr);
-        for (int j = 0; j < n; ++j) {
-            write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
-            const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
-            load_block<T, D>(p, bn, t1, off, kr, vr);
-            compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
-            br = bn;
-        }
+    // one register set: once a block sits in the LDS tiles its registers
+    // take the next block's loads, which are then in flight during the
+    // block's matrix work.  The load after the last block is of an empty
+    // block (no rows in range), which reads no memory.
+    const int n = wave < nblk ? (nblk - wave + WAVES - 1) / WAVES : 0;   // this wave's blocks
+    if (n == 0) return;
+    const int tw = t0 + wave * kBlk, tstep = WAVES * kBlk;
+    BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, tw, t1);
+    uint4 kr[L::LI], vr[L::LI];
+    load_block<T, D>(p, br, t1, off, kr, vr);
+    for (int j = 0; j < n; ++j) {
+        write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
+        const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
+        load_block<T, D>(p, bn, t1, off, kr, vr);
+        compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
+        br = bn;
     }
 }
 
@@ -561,8 +517,8 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     }
 }
 
-template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED, bool UNI>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4)))
+template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
@@ -604,7 +560,7 @@ partial_mfma_kernel(const PartialParams p) {
     uint32_t badmask = 0;
     if constexpr (UNI) {
         st.init(p.phi2);
-        scan_split<T, D, GMAX, WAVES, PF, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        scan_split<T, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
         const uint64_t bal = __ballot(st.bad);
         const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
         if (lane == 0) sm.bad[wave] = mine;
@@ -616,68 +572,48 @@ partial_mfma_kernel(const PartialParams p) {
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+            scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
             finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, badmask);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<T, D, GMAX, WAVES, PF, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
         finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all);
     }
     if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
 
-// Launch shape: waves per workgroup and whether a wave prefetches its next
-// block.  Chosen from measurements on MI355X.
-struct Shape {
-    int waves;
-    bool prefetch;
-};
-
-inline Shape launch_shape(const PartialParams &p) {
-    // 8-bit caches: a block is half the bytes for the same compute, so a wave
-    // without prefetch waits out a memory round trip per 4 KiB; always overlap
-    const bool f8 = p.dtype == FP8;
-    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B, per_cu4 = 4 * (int64_t)p.num_cus;
-    // more than four query rows per KV head in a grid of more than four
-    // workgroups per CU: one wave per workgroup (B=4, N=128k, G=8 and B=64
-    // paged batches measured no slower than with two); a grid the chip holds
-    // at once keeps two (32k GQA verifying 4 tokens, 16 rows)
-    if (p.R > 4 && wgs > per_cu4) return Shape{1, f8};
-    // fewer than four workgroups per CU: each SIMD runs one or two waves and a
-    // wave's own load-then-compute chain sets the pace, so overlap the two
-    // (Llama-2-7B-shaped MHA, 512 workgroups: 14.7 us against 15.5 us)
-    // (8-bit, 32k GQA: 2 waves 15.6 us, 4 waves 18.5 us -- 152 VGPRs leave
-    // room for 12 waves per CU, not the 16 that four 4-wave workgroups need)
-    return Shape{2, f8 || wgs < per_cu4};
+// Waves per workgroup, chosen from measurements on MI355X: more than four
+// query rows per KV head in a grid of more than four workgroups per CU take
+// one wave per workgroup (B=4, N=128k, G=8 and B=64 paged batches measured no
+// slower than with two); everything else takes two (32k GQA verifying 4
+// tokens, 16 rows: 28.8 us against 36.8 us with one; 32k GQA: 24.4 us
+// against 25.1-30.5 us with one, 24.9 us with four).
+inline int launch_waves(const PartialParams &p) {
+    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
+    return (p.R > 4 && wgs > 4 * (int64_t)p.num_cus) ? 1 : 2;
 }
 
-template <int T, int D, int GMAX, int WAVES, bool PF, bool PAGED>
+template <int T, int D, int GMAX, int WAVES, bool PAGED>
 hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
     dim3 grid(p.max_splits, p.Hkv, p.B);
     if (p.unified)
-        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, true>), grid, dim3(64 * WAVES), 0,
-                           stream, p);
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, true>), grid, dim3(64 * WAVES), 0, stream,
+                           p);
     else
-        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PF, PAGED, false>), grid, dim3(64 * WAVES), 0,
-                           stream, p);
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, false>), grid, dim3(64 * WAVES), 0, stream,
+                           p);
     return hipGetLastError();
 }
 
 template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
-    const Shape sh = launch_shape(p);
     if constexpr (GMAX > 4) {
-        if (sh.waves == 1) return launch_shaped<T, D, GMAX, 1, f8_of(T), PAGED>(p, stream);
+        if (launch_waves(p) == 1) return launch_shaped<T, D, GMAX, 1, PAGED>(p, stream);
     }
-    if constexpr (f8_of(T)) {
-        return launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream);
-    } else {
-        return sh.prefetch ? launch_shaped<T, D, GMAX, 2, true, PAGED>(p, stream)
-                           : launch_shaped<T, D, GMAX, 2, false, PAGED>(p, stream);
-    }
+    return launch_shaped<T, D, GMAX, 2, PAGED>(p, stream);
 }
 
 template <int T, int D, int GMAX>

@@ -186,10 +186,9 @@ def test_awkward_lengths(kernel, page):
     ft.check_partials(res, inp, 256, what=f"lengths page={page}")
 
 
-# both launch regimes of the MFMA kernel: a grid of fewer than four
-# workgroups per CU takes the prefetching two-wave shape, a larger one the
-# plain shape (groups above four heads: one wave); workgroups = splits of the
-# longest request x KV heads x requests, split 256
+# both launch regimes of the MFMA kernel: two waves per workgroup, one for
+# more than four query rows in a grid of more than four workgroups per CU;
+# workgroups = splits of the longest request x KV heads x requests, split 256
 REGIMES = [
     (16, 16, (4096, 3000)),                   # G=1, 512 workgroups
     (16, 16, (4096,) * 6 + (3001, 17)),       # G=1, 2048
