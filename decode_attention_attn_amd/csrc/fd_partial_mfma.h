@@ -30,7 +30,9 @@
 //      layout of S^T is the A-operand layout of P (head l % 16, tokens
 //      4 * (l / 16) + e), so the probabilities stay in registers; they enter
 //      as a 16-bit high part plus the 16-bit rounding of the fp32 residual
-//      (two MFMAs), which keeps the weights to about 14 bits or better.
+//      (two MFMAs), which keeps the weights to about 14 bits or better; with
+//      8-bit caches under the synchronized softmax, as one f16 operand
+//      rounded to nearest against f16 V tiles.
 //      B (lane j of lane group q: V[token 4q + k][dim j] of the slice) comes
 //      from the V tile with ds_read_b64_tr_b16, whose result is lane j,
 //      element k = element j % 4 of the 8-byte row addressed by lane 4k + j / 4
@@ -108,6 +110,15 @@ constexpr int kBlk = 16;   // tokens per MFMA block
 constexpr int kF8 = 16;
 __host__ __device__ constexpr int op_of(int T) { return T & 15; }
 __host__ __device__ constexpr bool f8_of(int T) { return T >= kF8; }
+
+// P x V operand type.  8-bit caches with the synchronized softmax take f16
+// for both operands: the widened V values are exact in f16 and every
+// probability lies in [0, 1], so one MFMA on P rounded to nearest f16
+// (relative error <= 2^-11, absolute <= 2^-25 below the normal range)
+// replaces the high/residual pair.  The unified-max softmax keeps the pair in
+// the cache's operand type, since e^{s - phi} may exceed f16's range.
+__host__ __device__ constexpr bool pv_single(int T, bool UNIFIED) { return f8_of(T) && !UNIFIED; }
+__host__ __device__ constexpr int pv_type(int T, bool UNIFIED) { return pv_single(T, UNIFIED) ? F16 : op_of(T); }
 
 // How a block's cache rows are loaded: 16 bytes per lane, LPR lanes per row.
 template <int T, int D>
@@ -298,7 +309,7 @@ __device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi)
 
 // A block's K and V registers -> the wave's LDS tiles (the registers are
 // free again afterwards).
-template <int T, int D, int GMAX, int WAVES>
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
 __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], const uint4 (&vr)[KLoad<T, D>::LI],
                                             MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
@@ -316,7 +327,7 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
         if constexpr (f8_of(T)) {   // this lane's 16 values are chunks 2 ch and 2 ch + 1
             uint4 k0, k1, v0, v1;
             widen_f8<DT>(kr[i], k0, k1);
-            widen_f8<DT>(vr[i], v0, v1);
+            widen_f8<pv_type(T, UNIFIED)>(vr[i], v0, v1);
             const int c = 2 * ch, ks = r & (C::LPR - 1), vs = 2 * (r & (C::LPR / 2 - 1));
             *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c ^ ks)) = k0;
             *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * ((c + 1) ^ ks)) = k1;
@@ -395,8 +406,14 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
     }
 
     // ---- O += P V on the matrix cores
+    constexpr int PT = pv_type(T, UNIFIED);
     s16x4 phi, plo;
-    split_probs<DT>(pr, phi, plo);
+    if constexpr (pv_single(T, UNIFIED)) {
+        const f16x4 ph = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+        phi = __builtin_bit_cast(s16x4, ph);
+    } else {
+        split_probs<DT>(pr, phi, plo);
+    }
     // this lane's 8-byte row of the transposing read: token 4 * mq + mrow / 4,
     // dims 16 * slice + 4 * (mrow % 4) .. + 3
     const int vrow = 4 * mq + (mrow >> 2);
@@ -408,8 +425,8 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
         const int slot = (dim >> 3) ^ vsw;
         const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
-        st.o[i] = mfma16x16x16<DT>(phi, bv, st.o[i]);
-        st.o[i] = mfma16x16x16<DT>(plo, bv, st.o[i]);
+        st.o[i] = mfma16x16x16<PT>(phi, bv, st.o[i]);
+        if constexpr (!pv_single(T, UNIFIED)) st.o[i] = mfma16x16x16<PT>(plo, bv, st.o[i]);
     }
 }
 
@@ -435,7 +452,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     uint4 kr[L::LI], vr[L::LI];
     load_block<T, D>(p, br, t1, off, kr, vr);
     for (int j = 0; j < n; ++j) {
-        write_tiles<T, D, GMAX, WAVES>(kr, vr, sm);
+        write_tiles<T, D, GMAX, WAVES, UNIFIED>(kr, vr, sm);
         const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
         load_block<T, D>(p, bn, t1, off, kr, vr);
         compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);

@@ -456,7 +456,11 @@ def test_fp8_cache_shapes(kernel, qdt, d, Hq, Hkv):
 @pytest.mark.parametrize("page", [0, 16])
 def test_fp8_cache_equals_the_bf16_cache_of_its_values_bitwise(kernel, page):
     """Power-of-two scales make the dequantised values exact bf16 numbers, and
-    the widening is exact: both caches give the same bits."""
+    the widening is exact: both caches give the same scores, hence the same
+    bits of m, l and lse.  The VALU kernel also gives the same O bits.  The
+    MFMA kernel takes P x V of an 8-bit cache in f16 (P rounded to nearest,
+    relative error <= 2^-11) where the 16-bit cache takes P as a bf16 pair
+    (<= 2^-14), so its O rows differ by at most about 2^-11 max|v|."""
     inp8 = _fp8_workload("fp8eq", 2, 32, 8, 128, "bf16", (3000, 517), page=page)
     w16 = dataclasses.replace(inp8.w, dtype="bf16", qdtype=None, k_scale=1.0, v_scale=1.0)
     k16 = synth.f32_to_bf16_bits((synth.decode_f64(inp8.k, "fp8") * inp8.w.k_scale).astype(np.float32))
@@ -464,10 +468,18 @@ def test_fp8_cache_equals_the_bf16_cache_of_its_values_bitwise(kernel, page):
     inp16 = synth.Inputs(w16, inp8.q, k16, v16, inp8.seq_lens, inp8.block_table)
     a = Run(inp8).run(kernel=kernel)
     b = Run(inp16).run(kernel=kernel)
-    for key in ("out", "lse", "part_m", "part_l"):
+    for key in ("lse", "part_m", "part_l"):
         assert np.array_equal(a[key], b[key]), key
     valid = a["part_l"] > 0
-    assert np.array_equal(a["part_o"][valid], b["part_o"][valid])
+    if kernel == "valu":
+        assert np.array_equal(a["out"], b["out"])
+        assert np.array_equal(a["part_o"][valid], b["part_o"][valid])
+    else:
+        vmax = float(np.nanmax(np.abs(synth.decode_f64(inp8.v, "fp8") * inp8.w.v_scale)))   # poisoned tail: NaN codes
+        tol = 2.0 ** -10 * vmax
+        assert np.abs(a["part_o"][valid] - b["part_o"][valid]).max() <= tol
+        # out is rounded to bf16 on top: at most one unit in the last place apart
+        assert np.abs(a["out"].astype(np.float64) - b["out"]).max() <= tol + 2.0 ** -7 * vmax
     ft.check_exact(a, inp8, what=f"fp8 {kernel} page={page}")
 
 
