@@ -335,8 +335,8 @@ def main():
         pmc_summary(args.workload, *args.pmc_summary, settings=run_settings(args))
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
-              f"MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the kernels run on the "
+              f"KV share of a single MI355X; there is no multi-GPU path)", file=sys.stderr)
         return 2
 
     import synth

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "fd_decode_attn.h"
@@ -229,17 +230,21 @@ FD_API fd_status fd_split_heuristic(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
     if (!split_size_out || !num_splits_out) return FD_ERR_INVALID_ARG;
     const int64_t unit = page_size > 0 ? page_size : 1;
     const int64_t n = max_seq_len > 0 ? max_seq_len : 1;
-    const int64_t work = (int64_t)B * Hkv;
+    const int64_t work = (int64_t)B * Hkv;                 // workgroups per split index
+    const int64_t cus = num_cus;
     int64_t split;
-    if (work >= 2 * (int64_t)num_cus) {
-        split = (n + unit - 1) / unit * unit;             // no split: one split covers the sequence
+    if (work * ((n + 255) / 256) <= 8 * cus) {
+        // at split 256 the grid fits on the GPU at once (<= 8 workgroups per
+        // CU): the page's granularity, aiming at about 2 workgroups per CU
+        const int64_t want = (2 * cus + work - 1) / work;   // splits per (request, KV head)
+        split = std::min<int64_t>(256, std::max<int64_t>(128, (n + want - 1) / want));
     } else {
-        const int64_t want = (2 * (int64_t)num_cus + work - 1) / work;   // splits per (request, KV head)
-        split = (n + want - 1) / want;
-        if (split < 128) split = 128;
-        if (split > 256) split = 256;
-        split = (split + unit - 1) / unit * unit;         // whole pages
+        // several waves of workgroups: every split costs a partial write, so
+        // grow the split up to 1024 while the grid keeps ~8 workgroups per CU
+        split = std::min<int64_t>(1024, std::max<int64_t>(256, (n * work + 8 * cus - 1) / (8 * cus)));
     }
+    split = std::max<int64_t>(split, (n + kMaxSplits - 1) / kMaxSplits);
+    split = (split + unit - 1) / unit * unit;             // whole pages
     if (split > kMaxSplitSize) split = (kMaxSplitSize / unit) * unit;
     if (split < 1) return FD_ERR_UNSUPPORTED;
     const int64_t S = (n + split - 1) / split;

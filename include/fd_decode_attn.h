@@ -73,7 +73,7 @@ extern "C" {
 typedef enum fd_status {
     FD_OK = 0,
     FD_ERR_INVALID_ARG = 1,          /* a NULL where a tensor is required, a bad size or range */
-    FD_ERR_UNSUPPORTED = 2,          /* a valid request this build has no kernel for */
+    FD_ERR_UNSUPPORTED = 2,          /* a valid request the library has no kernel for */
     FD_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < fd_workspace_bytes(desc) */
     FD_ERR_HIP = 4                   /* the HIP runtime rejected a launch */
 } fd_status;
@@ -172,11 +172,20 @@ fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q, const 
 size_t fd_workspace_bytes(const fd_decode_desc *desc);
 
 /* Host-only split choice, no GPU call.  Work units W = B * Hkv (one workgroup
- * covers a GQA group).  With W >= 2 * num_cus no split is needed and the split
- * is the whole (page-rounded) sequence; otherwise the split gives about
- * 2 * num_cus work units and is clamped to 128..256 tokens, rounded to whole
- * pages (Flash-Decoding page, "Production Implementation Guidelines", and
- * "Mathematical Formulation of Split-KV Parallelism" for S = ceil(N / split)).
+ * covers a GQA group), S256 = ceil(N / 256).
+ *   W * S256 <= 8 * num_cus (the grid fits on the GPU at once): the split
+ *     gives about 2 * num_cus workgroups, clamped to 128..256 tokens (the
+ *     Flash-Decoding page's granularity, "Production Implementation
+ *     Guidelines").
+ *   otherwise: split = ceil(N * W / (8 * num_cus)) clamped to 256..1024, so
+ *     the grid keeps about 8 workgroups per CU while writing fewer partials.
+ *     This departs from the page's "no split once B * H >= 2 * SMs" rule:
+ *     on MI355X one workgroup streams a (request, KV head) far slower than
+ *     the GPU's share of bandwidth, and partial writes interleaved with
+ *     saturated reads are expensive (measured: B=4, N=128k GQA 399 -> 353 us
+ *     per step at split 1024; B=64 ragged paged 495 -> 482 us).
+ * The split is then raised so that S <= 4096 and rounded up to whole pages;
+ * S = ceil(N / split) ("Mathematical Formulation of Split-KV Parallelism").
  * page_size 0 means a contiguous cache. */
 fd_status fd_split_heuristic(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
                              int32_t num_cus, int32_t *split_size_out, int32_t *num_splits_out);

@@ -189,7 +189,8 @@ WORKLOADS = {
     "long_gqa_32k": Workload("long_gqa_32k", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=32768),
     "paged_batched_gqa": Workload("paged_batched_gqa", B=64, Hq=64, Hkv=8, d=128, dtype="bf16", split=256,
                                   N=16384, len_range=(1024, 16384), page_size=16),
-    "umax_stress": Workload("umax_stress", B=4, Hq=64, Hkv=8, d=128, dtype="bf16", split=256, N=131072,
+    # no split size is given for this shape: 1024 is what the library's split heuristic picks for it
+    "umax_stress": Workload("umax_stress", B=4, Hq=64, Hkv=8, d=128, dtype="bf16", split=1024, N=131072,
                             stress_frac=0.02, stress_scale=8.0),
     # the long-context GQA shape with an 8-bit cache (scale 1/64: N(0, 1) draws stored as 64 x)
     "long_gqa_32k_fp8": Workload("long_gqa_32k_fp8", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256,

@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI that need no GPU: the library loads and
-exports every declared symbol, the split heuristic reproduces the pages'
-rules, and invalid arguments come back as status codes before anything is
+exports every declared symbol, the split heuristic follows the pages' rules
+where the grid fits on the GPU at once and its measured MI355X rule beyond, and invalid arguments come back as status codes before anything is
 launched.  Every call here either is host-only (the heuristic, the workspace
 size, status names) or fails validation, so no kernel is ever enqueued."""
 import ctypes as C
@@ -49,7 +49,8 @@ def test_desc_struct_matches_header_field_order():
 
 
 # ----------------------------------------------------------------------------
-# split heuristic: the Flash-Decoding page's dispatch and granularity rules
+# split heuristic: the Flash-Decoding page's granularity while the grid fits
+# on the GPU at once, larger splits (fewer partials) once it does not
 # ----------------------------------------------------------------------------
 MI355X_CUS = 256
 
@@ -58,24 +59,33 @@ MI355X_CUS = 256
     (1, 8, 8, 512, 0, 128, 4),          # tiny MHA
     (1, 32, 32, 4096, 0, 256, 16),      # Llama2-7B-shaped MHA
     (1, 32, 8, 32768, 0, 256, 128),     # long-context GQA
-    (4, 64, 8, 131072, 0, 256, 512),    # unified-max stress shape
+    (4, 64, 8, 131072, 0, 1024, 128),   # unified-max stress shape: 4096 workgroups at split 1024
 ])
 def test_heuristic_reproduces_the_workload_split_sizes(B, Hq, Hkv, N, page, split, S):
     assert fd.fd_split_heuristic(B, Hq, Hkv, N, page, MI355X_CUS) == (split, S)
 
 
-def test_heuristic_no_split_once_work_fills_the_gpu_twice():
-    # B * Hkv = 512 = 2 * 256 work units: the page's rule says no split
-    split, S = fd.fd_split_heuristic(64, 64, 8, 16384, 16, MI355X_CUS)
-    assert S == 1 and split == 16384
+def test_heuristic_grows_the_split_when_the_grid_is_several_waves():
+    # B * Hkv = 512 units, 64 splits of 256 each: 32768 workgroups.  The page
+    # would not split at all (512 >= 2 * CUs); here the split grows to the
+    # 1024-token cap, still 8192 workgroups at the longest length
+    assert fd.fd_split_heuristic(64, 64, 8, 16384, 16, MI355X_CUS) == (1024, 16)
+    # a batch that fills the GPU with short requests: one split per request
+    assert fd.fd_split_heuristic(256, 64, 8, 512, 16, MI355X_CUS) == (512, 1)
+    # between the two: the split that leaves ~8 workgroups per CU
+    split, S = fd.fd_split_heuristic(16, 64, 8, 8192, 16, MI355X_CUS)
+    assert split == 512 and S == 16 and 16 * 8 * S == 8 * MI355X_CUS
+    # a very long request: the split rises so that S stays within 4096
+    split, S = fd.fd_split_heuristic(1, 8, 1, 1 << 23, 0, MI355X_CUS)
+    assert (split, S) == (2048, 4096)
 
 
 def test_heuristic_page_example_split_count(golden):
     g = golden("flashdecoding_split_sizes.json")["split_count_example"]
     # the page's example: N = 32768, split 256 -> S = 128; with 16 query heads
     # at B = 1 that is 2048 blocks (one per query head); here a block covers a
-    # KV head, so use Hq = Hkv = 16
-    split, S = fd.fd_split_heuristic(g["B"], g["query_heads"], g["query_heads"], g["N"], 0, 108)
+    # KV head, so use Hq = Hkv = 16.  2048 workgroups fit on MI355X at once.
+    split, S = fd.fd_split_heuristic(g["B"], g["query_heads"], g["query_heads"], g["N"], 0, MI355X_CUS)
     assert split == g["split"] and S == g["S"]
     assert g["B"] * g["query_heads"] * S == g["blocks"]
 
@@ -84,13 +94,17 @@ def test_heuristic_page_example_split_count(golden):
 def test_heuristic_is_page_aligned_clamped_and_monotone(golden, page):
     gran = golden("flashdecoding_split_sizes.json")["split_granularity"]
     last_S = 0
-    for N in [1, 100, 1000, 4096, 10000, 32768, 100000, 131072]:
+    for N in [1, 100, 1000, 4096, 10000, 32768, 100000, 131072, 1 << 20]:
         split, S = fd.fd_split_heuristic(1, 32, 8, N, page, MI355X_CUS)
         assert split % page == 0
-        assert gran["lo"] <= split <= gran["hi"]
         assert S == -(-N // split)
         assert S >= last_S
         last_S = S
+        if 8 * -(-N // 256) <= 8 * MI355X_CUS:            # the grid fits at once: the page's range
+            assert gran["lo"] <= split <= gran["hi"]
+        else:                                            # several waves: ~8 workgroups per CU
+            assert 256 <= split <= 1024 + page
+            assert 8 * S >= 0.9 * 8 * MI355X_CUS or split >= 1024   # (page rounding)
 
 
 def test_heuristic_rejects_bad_arguments():
