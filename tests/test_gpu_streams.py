@@ -1,0 +1,123 @@
+"""The C ABI on streams other than the default one, and under HIP graph capture.
+
+The library enqueues every kernel on the stream it is given and allocates,
+clears and synchronises nothing itself, so a call on a side stream gives the
+same bits as on the default stream, and a captured call replays like an eager
+one.  The graph cases replay several times with new query values copied into
+the same buffer between replays, with eager work in between, and compare every
+replay bit for bit with an eager call on the same values (and one replay with
+the oracle).
+"""
+import numpy as np
+import pytest
+
+import fdtest as ft
+from fdtest import Run, say
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = ft.torch()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_attn_amd as fd
+    fd.lib()
+
+
+def _inputs(page):
+    base = synth.Workload("streams", B=3, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=page)
+    return synth.make_inputs(synth.with_lens(base, [4100, 517, 2049]))
+
+
+class _Call:
+    """One decode call (partial + combine, or the paged entry point) on fixed buffers."""
+
+    def __init__(self, r: Run):
+        import decode_attention_attn_amd as fd
+        t = ft.torch()
+        self.fd, self.r, w = fd, r, r.w
+        self.desc = r.desc()
+        self.out = t.empty((w.B, w.Hq, w.d), dtype=t.bfloat16, device="cuda")
+        self.lse = t.empty((w.B, w.Hq), dtype=t.float32, device="cuda")
+        if w.page_size:
+            self.ws = fd.alloc_workspace(self.desc)
+        else:
+            self.po, self.pm, self.pl, _ = fd.alloc_partials(self.desc)
+
+    def __call__(self, stream=None):
+        fd, r, w = self.fd, self.r, self.r.w
+        if w.page_size:
+            fd.fd_decode_attn_paged(self.desc, r.q, r.k, r.v, w.page_size, r.table, r.lens, self.ws, self.out,
+                                    self.lse, stream=stream)
+        else:
+            fd.fd_decode_attn_partial(self.desc, r.q, r.k, r.v, w.N, r.lens, self.po, self.pm, self.pl,
+                                      stream=stream)
+            fd.fd_decode_attn_combine(self.desc, self.po, self.pm, self.pl, r.lens, self.out, self.lse,
+                                      stream=stream)
+
+    def result(self):
+        w = self.r.w
+        R = w.B * w.Hq
+        return ft.f64(self.out).reshape(R, w.d), ft.f64(self.lse).reshape(R)
+
+
+@pytest.mark.parametrize("page", [0, 16])
+def test_side_stream_gives_the_default_stream_bits(page):
+    t = ft.torch()
+    inp = _inputs(page)
+    call = _Call(Run(inp))
+    call()
+    t.cuda.synchronize()
+    ref_out, ref_lse = call.result()
+    call.out.fill_(0)
+    call.lse.fill_(0)
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        call(stream=side)
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    out, lse = call.result()
+    assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
+    ft.check_exact(dict(out=out, lse=lse), inp, what=f"side stream page={page}")
+
+
+@pytest.mark.parametrize("page", [0, 16])
+def test_captured_call_replays_like_eager(page):
+    t = ft.torch()
+    inp = _inputs(page)
+    r = Run(inp)
+    call = _Call(r)
+    w = inp.w
+    qs = [synth.normal(900 + i, inp.q.shape, w.q_dtype) for i in range(3)]
+
+    # warm up on a side stream, then capture one call
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        call()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        call()
+    t.cuda.synchronize()
+
+    for i, qi in enumerate(qs):
+        r.q.copy_(ft.to_dev(qi, w.q_dtype))
+        call()                                   # eager on the same buffers
+        t.cuda.synchronize()
+        ref_out, ref_lse = call.result()
+        call.out.fill_(0)
+        call.lse.fill_(0)
+        graph.replay()
+        t.cuda.synchronize()
+        out, lse = call.result()
+        say(f"[graph page={page}] replay {i}: max|out - eager| = {np.abs(out - ref_out).max():.3e}")
+        assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse), f"replay {i}"
+        if i == len(qs) - 1:
+            ft.check_exact(dict(out=out, lse=lse), synth.Inputs(w, qi, inp.k, inp.v, inp.seq_lens,
+                                                                inp.block_table), what=f"graph page={page}")
