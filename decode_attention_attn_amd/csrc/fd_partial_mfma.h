@@ -133,10 +133,8 @@ template <int D, int GMAX, int WAVES>
 struct MCfg {
     static constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension (QK)
     static constexpr int SL = D / 16;                 // 16-dim output slices (PV)
-    static constexpr int LPR = D / 8;                 // lanes per row in the natural layout
-    static constexpr int RPI = 64 / LPR;              // rows per load instruction
-    static constexpr int LI = kBlk / RPI;             // load instructions per block
-    static constexpr int ROWB = D * 2;                // bytes per cache row
+    static constexpr int LPR = D / 8;                 // 16-byte chunks per 16-bit tile row
+    static constexpr int ROWB = D * 2;                // bytes per tile row
     static constexpr int THREADS = 64 * WAVES;
 };
 
@@ -602,15 +600,22 @@ partial_mfma_kernel(const PartialParams p) {
     if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
 
-// Waves per workgroup, chosen from measurements on MI355X: more than four
-// query rows per KV head in a grid of more than four workgroups per CU take
-// one wave per workgroup (B=4, N=128k, G=8 and B=64 paged batches measured no
-// slower than with two); everything else takes two (32k GQA verifying 4
-// tokens, 16 rows: 28.8 us against 36.8 us with one; 32k GQA: 24.4 us
-// against 25.1-30.5 us with one, 24.9 us with four).
+// Waves per workgroup, chosen from measurements on MI355X.  A grid of at
+// least four workgroups per CU takes one wave per workgroup when the cache is
+// 16-bit (32k GQA, 1024 workgroups: 24.3 us against 24.7 with two) or when
+// there are more than four query rows and the grid is larger than that (B=4,
+// N=128k, G=8 and B=64 paged batches: no slower than two).  Everything else
+// takes two: smaller grids need the second wave's loads in flight (Llama-2
+// shape, 512 workgroups: 14.6 us against 17.6 with one), 8-bit caches need
+// it to cover their heavier per-byte compute (32k GQA E4M3: 14.9 against
+// 19.4), and 32k GQA verifying 4 tokens (16 rows, 1024 workgroups) measured
+// 29.3-29.9 against 30.0-30.4 with one.
+template <int T>
 inline int launch_waves(const PartialParams &p) {
     const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
-    return (p.R > 4 && wgs > 4 * (int64_t)p.num_cus) ? 1 : 2;
+    const int64_t fill = 4 * (int64_t)p.num_cus;
+    if (p.R > 4) return wgs > fill ? 1 : 2;
+    return (!f8_of(T) && wgs >= fill) ? 1 : 2;
 }
 
 template <int T, int D, int GMAX, int WAVES, bool PAGED>
@@ -627,8 +632,8 @@ hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
 
 template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
-    if constexpr (GMAX > 4) {
-        if (launch_waves(p) == 1) return launch_shaped<T, D, GMAX, 1, PAGED>(p, stream);
+    if constexpr (GMAX > 4 || !f8_of(T)) {
+        if (launch_waves<T>(p) == 1) return launch_shaped<T, D, GMAX, 1, PAGED>(p, stream);
     }
     return launch_shaped<T, D, GMAX, 2, PAGED>(p, stream);
 }
