@@ -458,10 +458,11 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     }
 }
 
-// Wave states -> LDS -> the split's partial for the heads in write_mask.  The
-// P x V rows are already per head (lane group q holds heads 4q .. 4q + 3 of
-// one dim per slice, one 16-byte LDS store each); after one barrier each
-// thread merges one dim of four heads over the waves by the max-rescale rule.
+// Wave states -> the split's partial for the heads in write_mask.  One wave
+// writes its registers directly.  Several waves go through LDS: the P x V
+// rows are already per head (lane group q holds heads 4q .. 4q + 3 of one dim
+// per slice, one 16-byte LDS store each); after one barrier each thread
+// merges one dim of four heads over the waves by the max-rescale rule.
 template <int T, int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
                              int s, uint32_t write_mask) {
@@ -469,6 +470,30 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mrow = lane & 15, mq = lane >> 4;
+    if constexpr (WAVES == 1) {
+        // one wave holds the whole state: lane (mrow, mq) writes dim
+        // 16 * slice + mrow of rows 4 * mq + r straight from its registers,
+        // with l and m of those rows read from the lanes that hold them
+        float lsum = st.l + __shfl_xor(st.l, 16);
+        lsum += __shfl_xor(lsum, 32);
+        if (mq >= GQ) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * mq + r;
+            const float L = __shfl(lsum, g, 16), M = __shfl(st.m, g, 16);
+            if (g >= p.R || !((write_mask >> g) & 1u)) continue;
+            const size_t slot = row_slot(p, b, kvh, g, s);
+            float inv = L > 0.f ? 1.f / L : 0.f;
+            if constexpr (f8_of(T)) inv *= p.v_mult;   // a stored V unit stands for v_scale
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) p.part_o[slot * D + 16 * i + mrow] = st.o[i][r] * inv;
+            if (mrow == 0) {
+                p.part_m[slot] = (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY;
+                p.part_l[slot] = L;
+            }
+        }
+        return;
+    }
     __syncthreads();   // the epilogue area overlays the K tiles of every wave
     if (mq < GQ) {
 #pragma unroll
