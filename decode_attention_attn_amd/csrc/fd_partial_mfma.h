@@ -670,22 +670,21 @@ partial_mfma_kernel(const PartialParams p) {
     if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
 
-// Waves per workgroup, chosen from measurements on MI355X.  A grid of at
-// least four workgroups per CU takes one wave per workgroup when the cache is
-// 16-bit (32k GQA, 1024 workgroups: 24.3 us against 24.7 with two) or when
-// there are more than four query rows and the grid is larger than that (B=4,
-// N=128k, G=8 and B=64 paged batches: no slower than two).  Everything else
-// takes two: smaller grids need the second wave's loads in flight (Llama-2
-// shape, 512 workgroups: 14.6 us against 17.6 with one), 8-bit caches need
-// it to cover their heavier per-byte compute (32k GQA E4M3: 14.9 against
-// 19.4), and 32k GQA verifying 4 tokens (16 rows, 1024 workgroups) measured
-// 29.3-29.9 against 30.0-30.4 with one.
+// Waves per workgroup, chosen from measurements on MI355X.  A grid of fewer
+// than four workgroups per CU takes two, whose loads it needs in flight
+// (Llama-2 shape, 512 workgroups: 14.6 us against 17.6 with one).  From four
+// per CU a 16-bit cache takes one, which saves the hand-over between waves
+// (32k GQA, 1024 workgroups: 23.3 us against 25.2; verifying 4 tokens, 16
+// rows: 25.4-25.7 against 26.3; B=64 paged: 499 against 503; B=4, N=128k:
+// 352 against 349, the one shape measured the other way, by 1%).  An 8-bit
+// cache keeps two waves for up to four query rows, where the second wave
+// covers the widening (32k GQA E4M3: 14.7 us against 19.0 with one), and
+// takes one with more rows.
 template <int T>
 inline int launch_waves(const PartialParams &p) {
     const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
-    const int64_t fill = 4 * (int64_t)p.num_cus;
-    if (p.R > 4) return wgs > fill ? 1 : 2;
-    return (!f8_of(T) && wgs >= fill) ? 1 : 2;
+    if (wgs < 4 * (int64_t)p.num_cus) return 2;
+    return (!f8_of(T) || p.R > 4) ? 1 : 2;
 }
 
 template <int T, int D, int GMAX, int WAVES, bool PAGED>

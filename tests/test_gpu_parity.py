@@ -187,15 +187,14 @@ def test_awkward_lengths(kernel, page):
 
 
 # both launch regimes of the MFMA kernel on a 16-bit cache: one wave per
-# workgroup from four workgroups per CU (more than four, with more than four
-# query rows), two below; workgroups = splits of the longest request x KV
-# heads x requests, split 256, 256 CUs
+# workgroup from four workgroups per CU, two below; workgroups = splits of
+# the longest request x KV heads x requests, split 256, 256 CUs
 REGIMES = [
     (16, 16, (4096, 3000)),                   # G=1, 512 workgroups: two waves
     (16, 16, (4096,) * 6 + (3001, 17)),       # G=1, 2048: one
     (32, 8, (4096, 2900, 1)),                 # G=4, 384: two
     (32, 8, (4096,) * 7 + (100,)),            # G=4, 1024: one
-    (64, 8, (4096,) * 7 + (2500,)),           # G=8, 1024: two
+    (64, 8, (4096,) * 3 + (2500,)),           # G=8, 512: two
     (64, 8, (4096,) * 8 + (2500,)),           # G=8, 1152: one
 ]
 
