@@ -314,6 +314,27 @@ def test_paged_permutation_is_bitwise_invariant(kernel):
     ft.check_exact(r0, inp, what="perm")
 
 
+@pytest.mark.parametrize("kernel", ["auto"] + KERNELS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("page", [1, 8, 32, 64])
+def test_page_sizes(page, d, kernel):
+    """Pages of 1 to 64 tokens: the MFMA kernel takes pages of a multiple of
+    16 tokens and reports the others unsupported; auto falls back to the VALU
+    kernel there."""
+    import decode_attention_attn_amd as fd
+    base = synth.Workload("pages", B=3, Hq=16, Hkv=4, d=d, dtype="bf16", split=256, N=1, page_size=page)
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 257, 2048)))
+    what = f"page={page} d={d} {kernel}"
+    if kernel == "mfma" and page % 16:
+        with pytest.raises(fd.FdError) as e:
+            Run(inp).run(kernel=kernel)
+        assert e.value.status == fd.FD_ERR_UNSUPPORTED
+        return
+    res = Run(inp).run(kernel=kernel)
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 256, what=what)
+
+
 def test_paged_probe_reads_the_page_formula_location():
     """V rows encode their physical (block, slot) and one key per request is
     boosted so the softmax is one-hot; the output names the physical row."""
