@@ -310,6 +310,17 @@ __device__ __forceinline__ void widen_f8(const uint4 &raw, uint4 &lo, uint4 &hi)
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Tile slot of 16-byte chunk c before the row swizzle.  8-bit caches widen
+// 16 values per lane into chunks 2 ch and 2 ch + 1 of a row, so each of the
+// two stores covers every other chunk of the row; with 256-byte rows (d =
+// 128) chunks c and c + 8 share banks, and flipping bit 0 of the upper half
+// spreads a store's eight lanes over all of them.  The tiles of 16-bit caches
+// are written row-contiguous and need no flip.
+template <int T>
+__device__ __forceinline__ int chunk_slot(int c) {
+    return f8_of(T) ? c ^ ((c >> 3) & 1) : c;
+}
+
 // A block's K and V registers -> the wave's LDS tiles (the registers are
 // free again afterwards).
 template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
@@ -322,8 +333,8 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
     const int rg = lane / L::LPR, ch = lane % L::LPR;
     char *ktile = reinterpret_cast<char *>(sm.k[wave]);
     char *vtile = reinterpret_cast<char *>(sm.v[wave]);
-    // tiles: 16-byte chunk c of row r lives at slot c ^ (r & (LPR-1)) (K) and
-    // c ^ (2 * (r & (LPR/2 - 1))) (V), LPR = D / 8 chunks per row
+    // tiles: 16-byte chunk c of row r lives at slot chunk_slot(c) ^ (r & (LPR-1))
+    // (K) and chunk_slot(c) ^ (2 * (r & (LPR/2 - 1))) (V), LPR = D / 8 chunks per row
 #pragma unroll
     for (int i = 0; i < L::LI; ++i) {
         const int r = i * L::RPI + rg;
@@ -331,11 +342,12 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
             uint4 k0, k1, v0, v1;
             widen_f8<DT>(kr[i], k0, k1);
             widen_f8<pv_type(T, UNIFIED)>(vr[i], v0, v1);
-            const int c = 2 * ch, ks = r & (C::LPR - 1), vs = 2 * (r & (C::LPR / 2 - 1));
-            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c ^ ks)) = k0;
-            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * ((c + 1) ^ ks)) = k1;
-            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (c ^ vs)) = v0;
-            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * ((c + 1) ^ vs)) = v1;
+            const int c0 = chunk_slot<T>(2 * ch), c1 = chunk_slot<T>(2 * ch + 1);
+            const int ks = r & (C::LPR - 1), vs = 2 * (r & (C::LPR / 2 - 1));
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c0 ^ ks)) = k0;
+            *reinterpret_cast<uint4 *>(ktile + r * C::ROWB + 16 * (c1 ^ ks)) = k1;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (c0 ^ vs)) = v0;
+            *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (c1 ^ vs)) = v1;
         } else {                    // K chunks arrive pre-swizzled
             *reinterpret_cast<uint4 *>(ktile + i * L::RPI * C::ROWB + lane * 16) = kr[i];
             *reinterpret_cast<uint4 *>(vtile + r * C::ROWB + 16 * (ch ^ (2 * (r & (C::LPR / 2 - 1))))) = vr[i];
@@ -360,7 +372,7 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-        const int slot = (4 * ks + mq) ^ (mrow & (C::LPR - 1));
+        const int slot = chunk_slot<T>(4 * ks + mq) ^ (mrow & (C::LPR - 1));
         const uint4 a = *reinterpret_cast<const uint4 *>(ktile + mrow * C::ROWB + slot * 16);
         acc = mfma16x16x32<DT>(a, qop[ks], acc);
     }
@@ -425,7 +437,7 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
 #pragma unroll
     for (int i = 0; i < C::SL; ++i) {
         const int dim = 16 * i + 4 * (mrow & 3);
-        const int slot = (dim >> 3) ^ vsw;
+        const int slot = chunk_slot<T>(dim >> 3) ^ vsw;
         const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
         st.o[i] = mfma16x16x16<PT>(phi, bv, st.o[i]);
