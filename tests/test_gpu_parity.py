@@ -335,6 +335,69 @@ def test_page_sizes(page, d, kernel):
     ft.check_partials(res, inp, 256, what=what)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_paged_pool_beyond_4_gib(kernel):
+    """The requests' pages sit at the top of a pool of 4.3 GiB per cache (byte
+    offsets past 2^32); the rest of the pool is never written and must never
+    be read.  Same bits as the compact pool, and the oracle's values."""
+    t = ft.torch()
+    base = synth.Workload("bigpool", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=16)
+    inp = synth.make_inputs(synth.with_lens(base, (3000, 1500)))
+    small = Run(inp).run(kernel=kernel)
+    P = inp.k.shape[0]
+    P_big = 140_000                                   # 140000 pages of 32 KiB: 4.27 GiB per cache
+    shift = P_big - P
+    r = Run(inp)
+    big_k = t.empty((P_big,) + tuple(r.k.shape[1:]), dtype=r.k.dtype, device="cuda")
+    big_v = t.empty_like(big_k)
+    big_k[shift:] = r.k
+    big_v[shift:] = r.v
+    table = inp.block_table.copy()
+    table[table >= 0] += shift
+    r.k, r.v = big_k, big_v
+    r.table = t.from_numpy(table).to("cuda")
+    res = r.run(kernel=kernel)
+    for key in ("out", "lse", "part_m", "part_l"):
+        assert np.array_equal(res[key], small[key]), key
+    ft.check_exact(res, inp, what=f"pool beyond 4 GiB {kernel}")
+    del big_k, big_v
+    t.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_contiguous_cache_beyond_4_gib(kernel):
+    """Request 1 of a contiguous cache with 2^21 tokens of capacity starts
+    4 GiB into each cache; only the first len tokens of each request are
+    written.  Same bits as a cache of capacity N, and the oracle's values."""
+    import decode_attention_attn_amd as fd
+    t = ft.torch()
+    base = synth.Workload("bigcache", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", split=256, N=1)
+    inp = synth.make_inputs(synth.with_lens(base, (3000, 1500)))
+    w = inp.w
+    r = Run(inp)
+    small = r.run(kernel=kernel)
+    cap = 1 << 21                                     # 2^21 tokens x 2 KiB = 4 GiB per request
+    big_k = t.empty((w.B, cap, w.Hkv, w.d), dtype=r.k.dtype, device="cuda")
+    big_v = t.empty_like(big_k)
+    for b in range(w.B):
+        n = int(inp.seq_lens[b])
+        big_k[b, :n] = r.k[b, :n]
+        big_v[b, :n] = r.v[b, :n]
+    desc = r.desc(kernel=kernel)
+    po, pm, pl, _ = fd.alloc_partials(desc)
+    out = t.empty((w.B, w.Hq, w.d), dtype=t.bfloat16, device="cuda")
+    lse = t.empty((w.B, w.Hq), dtype=t.float32, device="cuda")
+    fd.fd_decode_attn_partial(desc, r.q, big_k, big_v, cap, r.lens, po, pm, pl)
+    fd.fd_decode_attn_combine(desc, po, pm, pl, r.lens, out, lse)
+    t.cuda.synchronize()
+    R = w.B * w.Hq
+    got_out, got_lse = ft.f64(out).reshape(R, w.d), ft.f64(lse).reshape(R)
+    assert np.array_equal(got_out, small["out"]) and np.array_equal(got_lse, small["lse"])
+    ft.check_exact(dict(out=got_out, lse=got_lse), inp, what=f"cache beyond 4 GiB {kernel}")
+    del big_k, big_v
+    t.cuda.empty_cache()
+
+
 def test_paged_probe_reads_the_page_formula_location():
     """V rows encode their physical (block, slot) and one key per request is
     boosted so the softmax is one-hot; the output names the physical row."""
