@@ -5,8 +5,10 @@ compares element by element with the oracle on the same inputs, at the bar
 stated in fdtest.py.  The five workload shapes run at full size (sampled rows
 for the two multi-GB ones, plus properties checked on every row); smaller
 cases cover the edges: ragged and empty requests, every dtype, head
-dimension and group size, split sizes from 1 token to a single split,
-poisoned cache tails, invalid page entries, and the unified-max fallback.
+dimension and group size, split sizes from 1 token to a single split, page
+sizes from 1 to 64 tokens, poisoned cache tails, invalid page entries, caches
+addressed beyond 4 GiB, both launch regimes of the MFMA kernel, 8-bit caches,
+several query tokens per request, and the unified-max fallback.
 """
 import dataclasses
 import math
