@@ -103,6 +103,17 @@ __device__ __forceinline__ void split_probs(const float (&pr)[4], s16x4 &hi, s16
 
 constexpr int kBlk = 16;   // tokens per MFMA block
 
+// Register budget and the order of the P x V operand reads, by query rows
+// per KV head (measured on MI355X, each A/B in one session).  Up to four
+// rows: at least 4 waves per SIMD (128 registers), each V slice read just
+// before its MFMAs (32k GQA: 23.4 us against 23.7 with the alternative).
+// More rows: at least 2 waves per SIMD, which leaves the compiler room to
+// read all V slices before the first MFMA (B=4, N=128k, 8 rows: 344.5 us
+// against 351.5; B=64 paged: 491.8 against 498.7; 4 query tokens of the 32k
+// GQA shape, 16 rows: 24.4 against 25.3).
+__host__ __device__ constexpr int min_waves_per_eu(int GMAX) { return GMAX > 4 ? 2 : 4; }
+__host__ __device__ constexpr bool batch_v_reads(int GMAX) { return GMAX > 4; }
+
 // Instantiation type T: the 16-bit operand type of the matrix instructions
 // (F16 or BF16, also the type of q), plus 16 when the cache holds 8-bit E4M3
 // values that are widened to it in registers (exactly: an E4M3 value has four
@@ -422,6 +433,24 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
 
     // ---- O += P V on the matrix cores
     constexpr int PT = pv_type(T, UNIFIED);
+    // this lane's 8-byte row of the transposing read: token 4 * mq + mrow / 4,
+    // dims 16 * slice + 4 * (mrow % 4) .. + 3
+    const int vrow = 4 * mq + (mrow >> 2);
+    const char *vrow_base = vtile + vrow * C::ROWB;
+    const int vsw = 2 * (vrow & (C::LPR / 2 - 1));
+    auto read_v = [&](int i) {
+        const int dim = 16 * i + 4 * (mrow & 3);
+        const int slot = chunk_slot<T>(dim >> 3) ^ vsw;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
+    };
+    // with batch_v_reads every slice is read before the first MFMA, so that
+    // the LDS latencies overlap; otherwise each just before its MFMAs
+    s16x4 bv[C::SL];
+    if constexpr (batch_v_reads(GMAX)) {
+#pragma unroll
+        for (int i = 0; i < C::SL; ++i) bv[i] = read_v(i);
+    }
     s16x4 phi, plo;
     if constexpr (pv_single(T, UNIFIED)) {
         const f16x4 ph = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
@@ -429,19 +458,11 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
     } else {
         split_probs<DT>(pr, phi, plo);
     }
-    // this lane's 8-byte row of the transposing read: token 4 * mq + mrow / 4,
-    // dims 16 * slice + 4 * (mrow % 4) .. + 3
-    const int vrow = 4 * mq + (mrow >> 2);
-    const char *vrow_base = vtile + vrow * C::ROWB;
-    const int vsw = 2 * (vrow & (C::LPR / 2 - 1));
 #pragma unroll
     for (int i = 0; i < C::SL; ++i) {
-        const int dim = 16 * i + 4 * (mrow & 3);
-        const int slot = chunk_slot<T>(dim >> 3) ^ vsw;
-        const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(vrow_base + slot * 16 + (dim & 7) * 2));
-        st.o[i] = mfma16x16x16<PT>(phi, bv, st.o[i]);
-        if constexpr (!pv_single(T, UNIFIED)) st.o[i] = mfma16x16x16<PT>(plo, bv, st.o[i]);
+        const s16x4 b = batch_v_reads(GMAX) ? bv[i] : read_v(i);
+        st.o[i] = mfma16x16x16<PT>(phi, b, st.o[i]);
+        if constexpr (!pv_single(T, UNIFIED)) st.o[i] = mfma16x16x16<PT>(plo, b, st.o[i]);
     }
 }
 
@@ -615,7 +636,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 }
 
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
 partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
