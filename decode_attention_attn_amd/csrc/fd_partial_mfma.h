@@ -153,19 +153,13 @@ template <int D, int GMAX, int WAVES>
 struct MSmem {
     using C = MCfg<D, GMAX, WAVES>;
     static constexpr int GQ = (GMAX + 3) / 4;      // head quads
-    struct Fin {
-        float4 acc[WAVES][D][GQ];                 // each wave's P x V rows: [dim][head quad]
-        float l[WAVES][GMAX];                     // each wave's l per query row
-        float m[WAVES][GMAX];
-    };
     struct Handover {                             // wave 1's state, lane for lane, for wave 0
         float4 o[D / 16][64];
         float l[16], m[16];
     };
     union {
         uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tiles ...
-        Fin fin;                                  // ... reused by the epilogue once every wave is done
-        Handover ho;
+        Handover ho;                              // ... reused by the epilogue once both waves are done
     };
     uint4 v[WAVES][kBlk * C::ROWB / 16];          // wave-private V tiles
     float corr[WAVES][16];                        // running-max rescale factors per head row
@@ -496,12 +490,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     }
 }
 
-// Wave states -> the split's partial for the heads in write_mask.  With one
-// or two waves, wave 0 writes from its registers (two: after merging the
-// state wave 1 hands over).  More waves go through LDS: the P x V rows are
-// already per head (lane group q holds heads 4q .. 4q + 3 of one dim per
-// slice, one 16-byte LDS store each); after one barrier each thread merges
-// one dim of four heads over the waves by the max-rescale rule.
+// Wave states -> the split's partial for the heads in write_mask.
 template <int T, int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
                              int s, uint32_t write_mask) {
@@ -509,128 +498,64 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mrow = lane & 15, mq = lane >> 4;
-    if constexpr (WAVES <= 2) {
-        // wave 0 writes the partial straight from its registers: lane
-        // (mrow, mq) holds dim 16 * slice + mrow of rows 4 * mq + r, and reads
-        // l and m of those rows from the lanes that hold them.  A second wave
-        // first hands its state over through LDS, lane for lane, and is merged
-        // in by the max-rescale rule.
-        float lsum = st.l + __shfl_xor(st.l, 16);
-        lsum += __shfl_xor(lsum, 32);
-        if constexpr (WAVES == 2) {
-            __syncthreads();   // the hand-over area overlays the K tiles of both waves
-            if (wave == 1) {
-                if (mq < GQ) {
-#pragma unroll
-                    for (int i = 0; i < C::SL; ++i)
-                        sm.ho.o[i][lane] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
-                }
-                if (mq == 0) {
-                    sm.ho.l[mrow] = lsum;
-                    sm.ho.m[mrow] = st.m;
-                }
-            }
-            __syncthreads();
-            if (wave == 1) return;
-        }
-        if (mq >= GQ) return;
-        float4 x[C::SL];
-        if constexpr (WAVES == 2) {
-#pragma unroll
-            for (int i = 0; i < C::SL; ++i) x[i] = sm.ho.o[i][lane];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = 4 * mq + r;
-            float L = __shfl(lsum, g, 16), M = __shfl(st.m, g, 16);
-            float f0 = 1.f, f1 = 0.f;
-            if constexpr (WAVES == 2) {
-                const float L1 = sm.ho.l[g], M1 = sm.ho.m[g];
-                const float Mx = fmaxf(M, M1);
-                f0 = rescale(M, Mx);
-                f1 = rescale(M1, Mx);
-                L = fmaf(L1, f1, L * f0);
-                M = Mx;
-            }
-            if (g >= p.R || !((write_mask >> g) & 1u)) continue;
-            const size_t slot = row_slot(p, b, kvh, g, s);
-            float inv = L > 0.f ? 1.f / L : 0.f;
-            if constexpr (f8_of(T)) inv *= p.v_mult;   // a stored V unit stands for v_scale
-#pragma unroll
-            for (int i = 0; i < C::SL; ++i) {
-                float a = st.o[i][r];
-                if constexpr (WAVES == 2) {
-                    const float xr = r == 0 ? x[i].x : r == 1 ? x[i].y : r == 2 ? x[i].z : x[i].w;
-                    a = fmaf(xr, f1, a * f0);
-                }
-                p.part_o[slot * D + 16 * i + mrow] = a * inv;
-            }
-            if (mrow == 0) {
-                p.part_m[slot] = (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY;
-                p.part_l[slot] = L;
-            }
-        }
-        return;
-    }
-    __syncthreads();   // the epilogue area overlays the K tiles of every wave
-    if (mq < GQ) {
-#pragma unroll
-        for (int i = 0; i < C::SL; ++i)
-            sm.fin.acc[wave][16 * i + mrow][mq] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
-    }
-    // the four lane groups hold l over different tokens of a row: sum them in
-    // registers, (g0 + g1) + (g2 + g3) in every lane
+    // wave 0 writes the partial straight from its registers: lane
+    // (mrow, mq) holds dim 16 * slice + mrow of rows 4 * mq + r, and reads
+    // l and m of those rows from the lanes that hold them.  A second wave
+    // first hands its state over through LDS, lane for lane, and is merged
+    // in by the max-rescale rule.
     float lsum = st.l + __shfl_xor(st.l, 16);
     lsum += __shfl_xor(lsum, 32);
-    if (mrow < GMAX && mq == 0) {
-        sm.fin.l[wave][mrow] = lsum;
-        sm.fin.m[wave][mrow] = st.m;
+    if constexpr (WAVES == 2) {
+        __syncthreads();   // the hand-over area overlays the K tiles of both waves
+        if (wave == 1) {
+            if (mq < GQ) {
+#pragma unroll
+                for (int i = 0; i < C::SL; ++i)
+                    sm.ho.o[i][lane] = make_float4(st.o[i][0], st.o[i][1], st.o[i][2], st.o[i][3]);
+            }
+            if (mq == 0) {
+                sm.ho.l[mrow] = lsum;
+                sm.ho.m[mrow] = st.m;
+            }
+        }
+        __syncthreads();
+        if (wave == 1) return;
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < GQ * D; idx += C::THREADS) {
-        const int gq = idx / D, dim = idx % D;
-        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-        float L[4] = {0.f, 0.f, 0.f, 0.f}, M[4];
+    if (mq >= GQ) return;
+    float4 x[C::SL];
+    if constexpr (WAVES == 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = 4 * gq + r;
-            M[r] = -INFINITY;
-            if (g < GMAX) {
+        for (int i = 0; i < C::SL; ++i) x[i] = sm.ho.o[i][lane];
+    }
 #pragma unroll
-                for (int w = 0; w < WAVES; ++w) M[r] = fmaxf(M[r], sm.fin.m[w][g]);
-            }
+    for (int r = 0; r < 4; ++r) {
+        const int g = 4 * mq + r;
+        float L = __shfl(lsum, g, 16), M = __shfl(st.m, g, 16);
+        float f0 = 1.f, f1 = 0.f;
+        if constexpr (WAVES == 2) {
+            const float L1 = sm.ho.l[g], M1 = sm.ho.m[g];
+            const float Mx = fmaxf(M, M1);
+            f0 = rescale(M, Mx);
+            f1 = rescale(M1, Mx);
+            L = fmaf(L1, f1, L * f0);
+            M = Mx;
         }
+        if (g >= p.R || !((write_mask >> g) & 1u)) continue;
+        const size_t slot = row_slot(p, b, kvh, g, s);
+        float inv = L > 0.f ? 1.f / L : 0.f;
+        if constexpr (f8_of(T)) inv *= p.v_mult;   // a stored V unit stands for v_scale
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float4 aw = sm.fin.acc[w][dim][gq];
-            float f[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int g = 4 * gq + r;
-                f[r] = 0.f;
-                if (g < GMAX) {
-                    f[r] = rescale(sm.fin.m[w][g], M[r]);
-                    L[r] = fmaf(sm.fin.l[w][g], f[r], L[r]);
-                }
+        for (int i = 0; i < C::SL; ++i) {
+            float a = st.o[i][r];
+            if constexpr (WAVES == 2) {
+                const float xr = r == 0 ? x[i].x : r == 1 ? x[i].y : r == 2 ? x[i].z : x[i].w;
+                a = fmaf(xr, f1, a * f0);
             }
-            A.x = fmaf(aw.x, f[0], A.x);
-            A.y = fmaf(aw.y, f[1], A.y);
-            A.z = fmaf(aw.z, f[2], A.z);
-            A.w = fmaf(aw.w, f[3], A.w);
+            p.part_o[slot * D + 16 * i + mrow] = a * inv;
         }
-        const float a4[4] = {A.x, A.y, A.z, A.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = 4 * gq + r;
-            if (g >= p.R || !((write_mask >> g) & 1u)) continue;
-            const size_t slot = row_slot(p, b, kvh, g, s);
-            float o = L[r] > 0.f ? a4[r] / L[r] : 0.f;
-            if constexpr (f8_of(T)) o *= p.v_mult;   // a stored V unit stands for v_scale
-            p.part_o[slot * D + dim] = o;
-            if (dim == 0) {
-                p.part_m[slot] = (L[r] > 0.f && M[r] != -INFINITY) ? M[r] * kLn2 : -INFINITY;
-                p.part_l[slot] = L[r];
-            }
+        if (mrow == 0) {
+            p.part_m[slot] = (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY;
+            p.part_l[slot] = L;
         }
     }
 }
@@ -639,6 +564,7 @@ template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
 partial_mfma_kernel(const PartialParams p) {
     using C = MCfg<D, GMAX, WAVES>;
+    static_assert(WAVES == 1 || WAVES == 2, "the epilogue merges at most two waves");
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
     const int kvh = blockIdx.y, b = blockIdx.z;
