@@ -46,11 +46,14 @@ __device__ float block_sum(float v, float *red) {
 }
 
 // One workgroup of THREADS threads merges DS of the D output dimensions of
-// one (request, query head); gridDim.z = D / DS slices.  No load waits for the
-// request length: O, m and l of all max_splits splits are requested at once
-// (rows past the request's last split are masked afterwards, never used),
-// so one memory round trip covers the inputs.
-template <int D, int DS, int THREADS>
+// one (request, query head); gridDim.z = D / DS slices.  SPEC: no load waits
+// for the request length; O, m and l of all max_splits splits are requested
+// at once (rows past the request's last split are masked afterwards, never
+// used), so one memory round trip covers the inputs.  Without SPEC the O rows
+// are requested once the length is known, only for the request's splits: one
+// more round trip, but no reads of rows a short request in a ragged batch
+// does not have.
+template <int D, int DS, int THREADS, bool SPEC>
 __global__ void __launch_bounds__(THREADS) combine_kernel(const CombineParams p) {
     extern __shared__ float sml[];         // [2][max_splits]: m, then l and finally the weights
     constexpr int DQ = DS / 4;             // threads per split row (float4 each)
@@ -70,20 +73,21 @@ __global__ void __launch_bounds__(THREADS) combine_kernel(const CombineParams p)
     const float *po = p.part_o + base * D + dim0;
     float *smm = sml, *sww = sml + Smax;
 
-    float4 o[JC];
-#pragma unroll
-    for (int j = 0; j < JC; ++j) {
-        const int s = sg + SG * j;
-        o[j] = s < Smax ? *reinterpret_cast<const float4 *>(po + (size_t)s * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    for (int s = threadIdx.x; s < Smax; s += THREADS) {
-        smm[s] = pm[s];
-        sww[s] = pl[s];
-    }
     int S = Smax;
     if (p.seq_lens) {
         const int len = request_len(p.seq_lens, b, Smax * p.split, Smax * p.split);
         S = (len + p.split - 1) / p.split;
+    }
+    const int Sload = SPEC ? Smax : S;
+    float4 o[JC];
+#pragma unroll
+    for (int j = 0; j < JC; ++j) {
+        const int s = sg + SG * j;
+        o[j] = s < Sload ? *reinterpret_cast<const float4 *>(po + (size_t)s * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int s = threadIdx.x; s < Smax; s += THREADS) {
+        smm[s] = pm[s];
+        sww[s] = pl[s];
     }
 
     float mx = -INFINITY;
@@ -145,11 +149,18 @@ __global__ void __launch_bounds__(THREADS) combine_kernel(const CombineParams p)
     if (threadIdx.x == 0 && slice == 0 && p.lse) p.lse[row] = lsum > 0.f ? mx + logf(lsum) : -INFINITY;
 }
 
+// Speculative O loads for a single request or when every request has the
+// full length; a batch with lengths reads only the rows it has.  Measured on
+// MI355X: B=64 ragged paged batch (lengths U[1024, 16384], 64 splits at most,
+// 34 on average) 492.6 -> 486.6 us per call; B=4 equal lengths unchanged.
 template <int D, int DS, int THREADS>
 hipError_t launch_shaped(const CombineParams &p, hipStream_t stream) {
     dim3 grid(p.Hq, p.B, D / DS);
     const size_t smem = 2 * (size_t)p.max_splits * sizeof(float);
-    hipLaunchKernelGGL((combine_kernel<D, DS, THREADS>), grid, dim3(THREADS), smem, stream, p);
+    if (p.B == 1 || !p.seq_lens)
+        hipLaunchKernelGGL((combine_kernel<D, DS, THREADS, true>), grid, dim3(THREADS), smem, stream, p);
+    else
+        hipLaunchKernelGGL((combine_kernel<D, DS, THREADS, false>), grid, dim3(THREADS), smem, stream, p);
     return hipGetLastError();
 }
 
