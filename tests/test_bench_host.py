@@ -1,0 +1,79 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU guard, the
+algorithmic byte counts the roofline divides by, and the HBM-counter scaling
+that turns rocprofv3's FETCH_SIZE / WRITE_SIZE into bytes per launch."""
+import csv
+import json
+import subprocess
+import sys
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import bench
+import synth
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout.strip() == ""
+
+
+def test_algorithmic_bytes_of_the_headline_shape():
+    # B=1, Hq=32, Hkv=8, d=128, N=32768, bf16: K and V of every (KV head, token)
+    # once, 2 * 128 * 2 = 512 bytes per unit, plus q (and out for the step)
+    inp = synth.make_inputs(synth.WORKLOADS["long_gqa_32k"], poison_tail=False)
+    a = bench.algorithmic_bytes(inp)
+    assert a["per_unit"] == 512 and a["units"] == 32768 * 8
+    assert a["kv"] == 32768 * 8 * 512
+    assert a["q"] == a["out"] == 32 * 128 * 2
+    assert a["partial"] == 134_225_920 and a["step"] == 134_225_920 + 8192 and a["table"] == 0
+
+
+def test_algorithmic_bytes_count_the_block_table_entries_read():
+    w = synth.with_lens(synth.Workload("t", B=3, Hq=8, Hkv=2, d=64, dtype="f16", split=64, N=1, page_size=16),
+                        (17, 16, 1000))
+    inp = synth.make_inputs(w, poison_tail=False)
+    a = bench.algorithmic_bytes(inp)
+    pages = 2 + 1 + 63
+    assert a["table"] == 4 * pages
+    assert a["kv"] == (17 + 16 + 1000) * 2 * 2 * 64 * 2
+    assert a["units"] == (17 + 16 + 1000) * 2
+
+
+def _write_counters(d: Path, counter, rows):
+    d.mkdir(parents=True)
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for i, (name, value) in enumerate(rows):
+            wr.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counter_bytes_are_scaled_by_the_calibration_copy(tmp_path, monkeypatch):
+    """A copy of COPY_BYTES reads as FETCH_SIZE = half its bytes and WRITE_SIZE
+    = all of them (the factors measured on MI355X); a kernel's counters scale by
+    the same factors, and only the first three copy dispatches calibrate."""
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    monkeypatch.setattr(bench, "source_hash", lambda: "h")
+    kib = bench.COPY_BYTES / 1024
+    partial = "void fd::partial_mfma_kernel<2, 128, 4, 1, false, false>(fd::PartialParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [(copy, kib / 2)] * 3 + [(copy, 5.0), (partial, 1000.0),
+                                                                           (partial, 1002.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [(copy, kib)] * 3 + [(copy, 7.0), (partial, 10.0), (partial, 10.0)])
+    settings = {"kernel": "auto", "mode": "sync"}
+    bench.pmc_summary("wl", tmp_path / "f", tmp_path / "w", settings)
+    d = json.loads((tmp_path / "profiles" / "wl_pmc.json").read_text())
+    assert d["fetch_scale"] == pytest.approx(2.0) and d["write_scale"] == pytest.approx(1.0)
+    expect = 1001.0 * 1024 * 2.0 + 10.0 * 1024 * 1.0
+    assert d["kernels"][bench.PARTIAL_KERNEL]["hbm_bytes_per_launch"] == pytest.approx(expect)
+    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, settings) == pytest.approx(expect)
+    # other settings, or other kernel sources, make the stored figure stale
+    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, {"kernel": "valu", "mode": "sync"}) is None
+    monkeypatch.setattr(bench, "source_hash", lambda: "changed")
+    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, settings) is None
