@@ -15,6 +15,7 @@
 namespace {
 
 using fd::kMaxGroup;
+using fd::kMaxRows;
 using fd::kMaxSplits;
 using fd::kMaxSplitSize;
 
@@ -25,8 +26,8 @@ fd_status validate_desc(const fd_decode_desc *d) {
     if (d->B < 0 || d->B > 65535 || d->Hq <= 0 || d->Hkv <= 0 || d->Hkv > 65535) return FD_ERR_INVALID_ARG;
     if (d->Hq % d->Hkv) return FD_ERR_INVALID_ARG;
     if (d->Hq / d->Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
-    if (d->q_len > kMaxGroup || (int64_t)(d->q_len > 1 ? d->q_len : 1) * (d->Hq / d->Hkv) > kMaxGroup)
-        return FD_ERR_UNSUPPORTED;   // a KV head's query rows must fit one 16-row matrix tile
+    if (d->q_len > kMaxRows || (int64_t)(d->q_len > 1 ? d->q_len : 1) * (d->Hq / d->Hkv) > kMaxRows)
+        return FD_ERR_UNSUPPORTED;   // a KV head's query rows must fit two 16-row matrix tiles
     if (d->d != 64 && d->d != 128) return FD_ERR_UNSUPPORTED;
     if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
     if (d->kv_dtype == FD_FP8_E4M3) {
@@ -105,6 +106,7 @@ fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t
     } else if (d->kernel == FD_KERNEL_AUTO) {
         mfma = fd::mfma_supports(p);
     }
+    if (!mfma && p.R > kMaxGroup) return FD_ERR_UNSUPPORTED;   // the VALU kernel holds up to 16 rows
     const hipError_t e = mfma ? fd::launch_partial_mfma(p, stream) : fd::launch_partial_valu(p, stream);
     return e == hipSuccess ? FD_OK : FD_ERR_HIP;
 }

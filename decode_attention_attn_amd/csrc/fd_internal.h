@@ -10,6 +10,7 @@ namespace fd {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxGroup = 16;       // query heads per KV head
+constexpr int kMaxRows = 32;        // query rows per KV head, q_len * G (MFMA kernel; VALU: 16)
 constexpr int kMaxSplits = 4096;    // the combine stages m and l of every split in LDS
 constexpr int kMaxSplitSize = 1 << 20;
 // unified max: |lo - phi|, |hi - phi| bound, so exp(s - phi) <= e^64 leaves

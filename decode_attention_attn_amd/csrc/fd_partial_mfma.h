@@ -5,7 +5,7 @@
 //
 // Work decomposition (as in the VALU kernel): one workgroup per (request b,
 // KV head, split s) covering all query rows of that KV head -- its G query
-// heads times the request's q_len query tokens, at most 16 -- so K and V are
+// heads times the request's q_len query tokens, at most 32 -- so K and V are
 // read from HBM once per group (handbook page "FlashAttention and inference
 // kernels", exercise 3).  Each wave walks 16-token blocks of the split.
 // 8-bit (E4M3) caches are widened exactly to the 16-bit operand type in
@@ -112,6 +112,10 @@ constexpr int kBlk = 16;   // tokens per MFMA block
 // against 351.5; B=64 paged: 491.8 against 498.7; 4 query tokens of the 32k
 // GQA shape, 16 rows: 24.4 against 25.3).
 __host__ __device__ constexpr int min_waves_per_eu(int GMAX) { return GMAX > 4 ? 2 : 4; }
+
+// 16-row tiles of query rows per KV head: the MFMA B operand holds 16 rows,
+// so up to 32 rows take two tiles that share each block's K and V tiles.
+__host__ __device__ constexpr int row_tiles(int GMAX) { return (GMAX + 15) / 16; }
 __host__ __device__ constexpr bool batch_v_reads(int GMAX) { return GMAX > 4; }
 
 // Instantiation type T: the 16-bit operand type of the matrix instructions
@@ -462,10 +466,12 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
 
 // One wave's share of the split: blocks wave, wave + WAVES, ...  Paged caches
 // read the split's block-table entries once (one per lane) and pick each
-// block's page from them with a lane read.
+// block's page from them with a lane read.  Each block runs through the
+// matrix work once per 16-row tile of query rows.
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, int lim, const uint4 (&qop)[D / 32],
-                           MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm) {
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1,
+                           const int (&lim)[row_tiles(GMAX)], const uint4 (&qop)[row_tiles(GMAX)][D / 32],
+                           MState<D, GMAX> (&st)[row_tiles(GMAX)], MSmem<D, GMAX, WAVES> &sm) {
     using L = KLoad<T, D>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const auto off = lane_offsets<T, D>(p);
@@ -485,17 +491,20 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
         write_tiles<T, D, GMAX, WAVES, UNIFIED>(kr, vr, sm);
         const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
         load_block<T, D>(p, bn, t1, off, kr, vr);
-        compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim, qop, st, sm);
+#pragma unroll
+        for (int rt = 0; rt < row_tiles(GMAX); ++rt)
+            compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim[rt], qop[rt], st[rt], sm);
         br = bn;
     }
 }
 
-// Wave states -> the split's partial for the heads in write_mask.
+// Wave states of row tile rt (query rows 16 rt ..) -> the split's partial
+// for the rows in write_mask.
 template <int T, int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
-                             int s, uint32_t write_mask) {
+                             int s, uint32_t write_mask, int rt) {
     using C = MCfg<D, GMAX, WAVES>;
-    constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ;
+    constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ < 4 ? MSmem<D, GMAX, WAVES>::GQ : 4;   // head quads per tile
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mrow = lane & 15, mq = lane >> 4;
     // wave 0 writes the partial straight from its registers: lane
@@ -529,11 +538,11 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int g = 4 * mq + r;
-        float L = __shfl(lsum, g, 16), M = __shfl(st.m, g, 16);
+        const int gl = 4 * mq + r, g = 16 * rt + gl;     // row within the tile, query row
+        float L = __shfl(lsum, gl, 16), M = __shfl(st.m, gl, 16);
         float f0 = 1.f, f1 = 0.f;
         if constexpr (WAVES == 2) {
-            const float L1 = sm.ho.l[g], M1 = sm.ho.m[g];
+            const float L1 = sm.ho.l[gl], M1 = sm.ho.m[gl];
             const float Mx = fmaxf(M, M1);
             f0 = rescale(M, Mx);
             f1 = rescale(M1, Mx);
@@ -584,47 +593,61 @@ partial_mfma_kernel(const PartialParams p) {
         return;
     }
 
+    constexpr int NT = row_tiles(GMAX);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // B operand: q of query row (lane % 16), dims 8 * (lane / 16) of each step
-    uint4 qop[C::KS];
-    const int lim = row_limit(p, len, t1, lane & 15);
-    {
-        const int rho = lane & 15;
+    // B operand of tile rt: q of query row 16 rt + lane % 16, dims 8 * (lane / 16)
+    // of each step; lim[rt]: that row's causal limit
+    uint4 qop[NT][C::KS];
+    int lim[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        const int rho = 16 * rt + (lane & 15);
+        lim[rt] = row_limit(p, len, t1, rho);
         const char *qb = static_cast<const char *>(p.q);
         const size_t qrow = rho < R ? query_row(p, b, kvh, rho) : 0;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            qop[ks] = make_uint4(0, 0, 0, 0);
-            if (rho < R) qop[ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
+            qop[rt][ks] = make_uint4(0, 0, 0, 0);
+            if (rho < R) qop[rt][ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
         }
     }
 
-    const uint32_t all = (1u << R) - 1u;
-    MState<D, GMAX> st;
+    const uint32_t all = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
+    MState<D, GMAX> st[NT];
     uint32_t badmask = 0;
     if constexpr (UNI) {
-        st.init(p.phi2);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) st[rt].init(p.phi2);
         scan_split<T, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
-        const uint64_t bal = __ballot(st.bad);
-        const uint32_t mine = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu);
+        uint32_t mine = 0;
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const uint64_t bal = __ballot(st[rt].bad);
+            mine |= (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu) << (16 * rt);
+        }
         if (lane == 0) sm.bad[wave] = mine;
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
         badmask &= all;
-        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all & ~badmask);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, all & ~badmask, rt);
         if (badmask) {   // synchronized recompute of the flagged heads
             __syncthreads();
-            st.init(-INFINITY);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
             scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
-            finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, badmask);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, badmask, rt);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
-        st.init(-INFINITY);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
         scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
-        finish_split<T, D, GMAX, WAVES>(p, st, sm, b, kvh, s, all);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, all, rt);
     }
     if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
 }
@@ -677,7 +700,8 @@ hipError_t by_group(const PartialParams &p, hipStream_t s) {
     if (p.R <= 2) return by_paged<T, D, 2>(p, s);
     if (p.R <= 4) return by_paged<T, D, 4>(p, s);
     if (p.R <= 8) return by_paged<T, D, 8>(p, s);
-    return by_paged<T, D, 16>(p, s);
+    if (p.R <= 16) return by_paged<T, D, 16>(p, s);
+    return by_paged<T, D, 32>(p, s);
 }
 
 template <int T>

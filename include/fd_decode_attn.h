@@ -32,7 +32,9 @@
  *    FlashAttention forward kernel, page "FlashAttention and inference
  *    kernels", section "FlashAttention: tiling plus online softmax").  Every
  *    per-head shape below is per query row: out [B, q_len, Hq, d], lse, m, l
- *    and flags [B, q_len, Hq, ...].  q_len * (Hq / Hkv) <= 16.
+ *    and flags [B, q_len, Hq, ...].  q_len * (Hq / Hkv) <= 32; more than 16 rows
+ *    per KV head need the MFMA kernel (the VALU kernel reports them
+ *    FD_ERR_UNSUPPORTED).
  *  - 8-bit caches (FD_FP8_E4M3, OCP FP8 E4M3: bias 7, no infinities, largest
  *    finite 448, S.1111.111 = NaN) stand for stored * k_scale and
  *    stored * v_scale (one scale per tensor); the handbook page lists caches

@@ -198,6 +198,9 @@ WORKLOADS = {
     # the long-context GQA shape verifying 4 drafted tokens (4 x 4 query rows per KV head)
     "long_gqa_32k_verify4": Workload("long_gqa_32k_verify4", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256,
                                      N=32768, q_len=4),
+    # the same with 8 drafted tokens: 32 query rows per KV head, two 16-row tiles
+    "long_gqa_32k_verify8": Workload("long_gqa_32k_verify8", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256,
+                                     N=32768, q_len=8),
 }
 
 

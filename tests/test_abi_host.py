@@ -201,10 +201,14 @@ def test_fp8_descriptor_validation():
 
 
 def test_multi_query_descriptor_validation():
-    """q_len * (Hq / Hkv) query rows of a KV head must fit one 16-row tile."""
+    """q_len * (Hq / Hkv) query rows of a KV head must fit two 16-row tiles
+    (INVALID_ARG below only says validation passed: the test hands no tensors);
+    more than 16 rows need the MFMA kernel."""
     assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=4)) == fd.FD_ERR_INVALID_ARG
-    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=5)) == fd.FD_ERR_UNSUPPORTED
-    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=17)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=8)) == fd.FD_ERR_INVALID_ARG
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=9)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=32)) == fd.FD_ERR_INVALID_ARG
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=33)) == fd.FD_ERR_UNSUPPORTED
     one = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4)
     zero = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=0)
     four = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=4)

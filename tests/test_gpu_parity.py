@@ -611,6 +611,9 @@ MQ_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d)
     ("mfma", "bf16", 24, 8, 5, 128), ("mfma", "fp8", 32, 8, 4, 128), ("mfma", "bf16", 16, 4, 3, 64),
     ("valu", "f32", 16, 8, 3, 128), ("valu", "bf16", 32, 8, 4, 128), ("valu", "fp8", 8, 8, 2, 128),
     ("valu", "f16", 8, 2, 4, 64),
+    # more than 16 rows: two 16-row tiles per KV head (MFMA kernel only)
+    ("mfma", "bf16", 64, 8, 4, 128), ("mfma", "f16", 24, 8, 7, 64), ("mfma", "fp8", 32, 4, 3, 128),
+    ("mfma", "bf16", 8, 8, 32, 128),
 ]
 
 
@@ -633,10 +636,27 @@ def test_multi_query_causal(kernel, dtype, Hq, Hkv, q_len, d, page):
         assert np.all(res["out"][r0:r0 + Hq] == 0.0) and np.all(res["lse"][r0:r0 + Hq] == -np.inf)
 
 
+def test_more_than_16_rows_need_the_mfma_kernel():
+    import decode_attention_attn_amd as fd
+    base = synth.Workload("mq32", B=1, Hq=64, Hkv=8, d=128, dtype="bf16", split=128, N=1, q_len=4)
+    inp = synth.make_inputs(synth.with_lens(base, (700,)))
+    with pytest.raises(fd.FdError) as e:
+        Run(inp).run(kernel="valu")
+    assert e.value.status == fd.FD_ERR_UNSUPPORTED
+    f32 = synth.make_inputs(synth.with_lens(dataclasses.replace(base, dtype="f32"), (700,)))
+    with pytest.raises(fd.FdError) as e:                # auto: no kernel for 32 fp32 rows
+        Run(f32).run()
+    assert e.value.status == fd.FD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("q_len,Hq", [(4, 16), (4, 64)])
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_multi_query_unified_max(kernel):
-    base = synth.Workload("mqu", B=1, Hq=16, Hkv=4, d=128, dtype="bf16", split=256, N=1, q_len=4,
-                          stress_frac=0.02, stress_scale=8.0)
+def test_multi_query_unified_max(kernel, q_len, Hq):
+    Hkv = 4 if Hq == 16 else 8
+    if kernel == "valu" and q_len * (Hq // Hkv) > 16:
+        pytest.skip("the VALU kernel holds up to 16 rows")
+    base = synth.Workload("mqu", B=1, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", split=256, N=1,
+                          q_len=q_len, stress_frac=0.02, stress_scale=8.0)
     inp = synth.make_inputs(synth.with_lens(base, (3000, 700)))
     w = inp.w
     S = -(-w.N // w.split)
@@ -646,7 +666,7 @@ def test_multi_query_unified_max(kernel):
     got = res["flags"].astype(bool)
     assert np.all(got[must]) and not np.any(got[~may])
     assert res["count"] == int(got.sum()) and 0 < got.sum() < got.size
-    ft.check_exact(res, inp, what=f"q_len=4 unified {kernel}")
+    ft.check_exact(res, inp, what=f"q_len={q_len} Hq={Hq} unified {kernel}")
 
 
 def test_multi_query_rows_match_single_query_runs_bitwise():
@@ -670,14 +690,15 @@ def test_multi_query_rows_match_single_query_runs_bitwise():
             assert np.array_equal(res["out"][r], r1["out"]), (b, i)
 
 
-def test_verify_4_tokens_long_context_gqa_full():
-    w = synth.WORKLOADS["long_gqa_32k_verify4"]
-    say("[long_gqa_32k_verify4] generating")
+@pytest.mark.parametrize("name", ["long_gqa_32k_verify4", "long_gqa_32k_verify8"])
+def test_verify_tokens_long_context_gqa_full(name):
+    w = synth.WORKLOADS[name]
+    say(f"[{name}] generating")
     inp = synth.make_inputs(w)
     res = Run(inp).run()
-    e1, e2 = ft.check_exact(res, inp, what="long_gqa_32k_verify4")
-    ft.check_partials(res, inp, w.split, what="long_gqa_32k_verify4")
-    say(f"[long_gqa_32k_verify4] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+    e1, e2 = ft.check_exact(res, inp, what=name)
+    ft.check_partials(res, inp, w.split, what=name)
+    say(f"[{name}] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
 
 
 # ----------------------------------------------------------------------------
