@@ -569,6 +569,24 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
     }
 }
 
+// KV head of grid row y.  Consecutive workgroups go to the eight XCDs in
+// turn, and an XCD hands its share to its CUs round by round, so in grid order
+// a grid that is resident at once with two workgroups per CU (32 KV heads, 16
+// splits: 512 workgroups) gives each CU the workgroups of heads h and
+// h + Hkv / 2, of equal parity; the odd heads, whose rows start at an odd
+// multiple of 256 bytes of each token row, ran ~10% slower in traces.  Such
+// grids take the odd heads first, which pairs one odd and one even head on
+// each CU.  Measured on MI355X at the Llama-2 shape: 14.0 -> 13.6 us; grids
+// with four workgroups per CU are unchanged (32k GQA, 1024 workgroups) and a
+// grid several waves deep is slower (B=4, N=128k: 351 against 358 us), so
+// those keep grid order.
+__device__ __forceinline__ int kv_head_of(const PartialParams &p, int y) {
+    const int wgs = (int)(gridDim.x * gridDim.y * gridDim.z);
+    if ((p.Hkv & 1) || wgs >= 4 * p.num_cus) return y;
+    const int half = p.Hkv >> 1;
+    return y < half ? 2 * y + 1 : 2 * (y - half);
+}
+
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
 partial_mfma_kernel(const PartialParams p) {
@@ -576,7 +594,7 @@ partial_mfma_kernel(const PartialParams p) {
     static_assert(WAVES == 1 || WAVES == 2, "the epilogue merges at most two waves");
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = kv_head_of(p, blockIdx.y), b = blockIdx.z;
     const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
     const int R = p.R;                               // query rows of this KV head
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
