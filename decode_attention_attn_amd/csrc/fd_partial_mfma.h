@@ -576,10 +576,11 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 // h + Hkv / 2, of equal parity; the odd heads, whose rows start at an odd
 // multiple of 256 bytes of each token row, ran ~10% slower in traces.  Such
 // grids take the odd heads first, which pairs one odd and one even head on
-// each CU.  Measured on MI355X at the Llama-2 shape: 14.0 -> 13.6 us; grids
-// with four workgroups per CU are unchanged (32k GQA, 1024 workgroups) and a
-// grid several waves deep is slower (B=4, N=128k: 351 against 358 us), so
-// those keep grid order.
+// each CU.  Measured on MI355X at the Llama-2 shape: 13.7-14.1 -> 13.2-13.6
+// us on two devices, within 1% on a third (as were resident GQA grids of 256
+// and 512 workgroups there); grids with four workgroups per CU are unchanged
+// (32k GQA, 1024 workgroups) and a grid several waves deep is slower (B=4,
+// N=128k: 351 against 358 us), so those keep grid order.
 __device__ __forceinline__ int kv_head_of(const PartialParams &p, int y) {
     const int wgs = (int)(gridDim.x * gridDim.y * gridDim.z);
     if ((p.Hkv & 1) || wgs >= 4 * p.num_cus) return y;
