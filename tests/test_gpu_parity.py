@@ -150,7 +150,9 @@ def test_umax_stress_full():
 # ----------------------------------------------------------------------------
 # dtype x head dim x group size x kernel on ragged requests
 # ----------------------------------------------------------------------------
-GROUPS = [(8, 8), (8, 4), (12, 4), (16, 2), (32, 2)]      # G = 1, 2, 3, 8, 16
+# G = 1, 2, 3, 8, 16, and 3 with an odd KV head count (whose resident grids keep grid-order heads;
+# even counts take the odd heads first)
+GROUPS = [(8, 8), (8, 4), (12, 4), (16, 2), (32, 2), (9, 3)]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
