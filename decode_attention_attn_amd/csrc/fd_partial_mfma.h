@@ -582,7 +582,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
 // (32k GQA, 1024 workgroups) and a grid several waves deep is slower (B=4,
 // N=128k: 351 against 358 us), so those keep grid order.
 __device__ __forceinline__ int kv_head_of(const PartialParams &p, int y) {
-    const int wgs = (int)(gridDim.x * gridDim.y * gridDim.z);
+    const int64_t wgs = (int64_t)gridDim.x * gridDim.y * gridDim.z;
     if ((p.Hkv & 1) || wgs >= 4 * p.num_cus) return y;
     const int half = p.Hkv >> 1;
     return y < half ? 2 * y + 1 : 2 * (y - half);
