@@ -268,8 +268,11 @@ def _cpu_model():
 
 def cpu_baseline(inp, alg, seconds):
     """The fp64 oracle, as it is, on the host cores: whole decode steps of the
-    same workload repeated until about `seconds` of work have run (all host
-    threads), then a shorter single-thread sample of the same rows."""
+    same workload repeated until about `seconds` of work have run, on one
+    thread per CPU the process may use (within OMP_NUM_THREADS where the host
+    sets it), then a shorter single-thread sample of the same rows.  `cores`
+    is the thread count used; `host_cpus` gives nproc, the affinity mask and
+    the thread limit it came from."""
     import oracle
     p = oracle.problem_of(inp)
     threads = oracle.default_threads()
@@ -299,6 +302,7 @@ def cpu_baseline(inp, alg, seconds):
     reps1, el1 = timed_rows(rows[:n1], 1, seconds / 4)
     step1_s = el1 / reps1 * (R / n1)
     return {"value": alg["step"] / step_s / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
+            "host_cpus": oracle.host_cpus(),
             "us_per_step": step_s * 1e6, "single_thread_us_per_step": step1_s * 1e6, "cpu": _cpu_model(),
             "sample": f"{reps} x {n_rows}/{R} query rows of the same workload, {el:.1f} s of fp64 oracle work "
                       f"on {threads} threads, scaled to one step; single thread: {reps1} x {n1} rows, {el1:.1f} s"}

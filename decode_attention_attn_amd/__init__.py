@@ -125,7 +125,7 @@ def _qdtype(desc):
     return _tdtype(desc.q_dtype if desc.kv_dtype == FD_FP8_E4M3 else desc.kv_dtype)
 
 
-def _ptr(t, name, dtype=None, numel=None, optional=False):
+def _ptr(t, name, dtype=None, numel=None, optional=False, align=16):
     if t is None:
         if optional:
             return None
@@ -141,8 +141,8 @@ def _ptr(t, name, dtype=None, numel=None, optional=False):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
-    if t.data_ptr() % 16:
-        raise ValueError(f"{name} must be 16-byte aligned")
+    if t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
     return C.c_void_p(t.data_ptr())
 
 
@@ -180,12 +180,12 @@ def fd_decode_attn_partial(desc, q, k, v, kv_capacity, seq_lens, part_o, part_m,
         _ptr(k, "k", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         _ptr(v, "v", kvt, desc.B * kv_capacity * desc.Hkv * desc.d),
         C.c_int32(int(kv_capacity)),
-        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, optional=True),
+        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, optional=True, align=4),
         _ptr(part_o, "part_o", torch.float32, nrow * desc.d),
-        _ptr(part_m, "part_m", torch.float32, nrow),
-        _ptr(part_l, "part_l", torch.float32, nrow),
-        _ptr(flags, "flags", torch.uint8, nrow, optional=True),
-        _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True),
+        _ptr(part_m, "part_m", torch.float32, nrow, align=4),
+        _ptr(part_l, "part_l", torch.float32, nrow, align=4),
+        _ptr(flags, "flags", torch.uint8, nrow, optional=True, align=1),
+        _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True, align=4),
         _stream(stream),
     ]
     _check("fd_decode_attn_partial", lib().fd_decode_attn_partial(C.byref(desc), *args))
@@ -196,11 +196,11 @@ def fd_decode_attn_combine(desc, part_o, part_m, part_l, seq_lens, out, lse=None
     nrow = desc.B * query_rows(desc) * desc.max_splits
     args = [
         _ptr(part_o, "part_o", torch.float32, nrow * desc.d),
-        _ptr(part_m, "part_m", torch.float32, nrow),
-        _ptr(part_l, "part_l", torch.float32, nrow),
-        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, optional=True),
+        _ptr(part_m, "part_m", torch.float32, nrow, align=4),
+        _ptr(part_l, "part_l", torch.float32, nrow, align=4),
+        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, optional=True, align=4),
         _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * query_rows(desc) * desc.d),
-        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True),
+        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True, align=4),
         _stream(stream),
     ]
     _check("fd_decode_attn_combine", lib().fd_decode_attn_combine(C.byref(desc), *args))
@@ -227,15 +227,15 @@ def fd_decode_attn_paged(desc, q, k_cache, v_cache, page_size, block_table, seq_
         _ptr(k_cache, "k_cache", kvt),
         _ptr(v_cache, "v_cache", kvt),
         C.c_int32(num_pages), C.c_int32(int(page_size)),
-        _ptr(block_table, "block_table", torch.int32),
+        _ptr(block_table, "block_table", torch.int32, align=4),
         C.c_int32(int(block_table.shape[1])),
-        _ptr(seq_lens, "seq_lens", torch.int32, desc.B),
-        _ptr(workspace, "workspace"),
+        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, align=4),
+        _ptr(workspace, "workspace", align=256),
         C.c_size_t(workspace.numel() * workspace.element_size()),
         _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * query_rows(desc) * desc.d),
-        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True),
-        _ptr(flags, "flags", torch.uint8, nrow, optional=True),
-        _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True),
+        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True, align=4),
+        _ptr(flags, "flags", torch.uint8, nrow, optional=True, align=1),
+        _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True, align=4),
         _stream(stream),
     ]
     _check("fd_decode_attn_paged", lib().fd_decode_attn_paged(C.byref(desc), *args))

@@ -113,6 +113,21 @@ fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Alignment of a base pointer (NULL passes: optional tensors are checked for
+// presence elsewhere).  Tensors read or written 16 bytes at a time (q, K, V,
+// part_o, out) need 16 bytes; the others their element size.
+bool aligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+bool aligned_partials(const float *part_o, const float *part_m, const float *part_l) {
+    return aligned(part_o, 16) && aligned(part_m, 4) && aligned(part_l, 4);
+}
+
+bool aligned_io(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                const int32_t *seq_lens, const int32_t *fallback_count) {
+    return aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(out, 16) && aligned(lse, 4) &&
+           aligned(seq_lens, 4) && aligned(fallback_count, 4);
+}
+
 struct WorkspaceLayout {
     size_t o_bytes, m_bytes, total;
 };
@@ -155,6 +170,9 @@ FD_API fd_status fd_decode_attn_partial(const fd_decode_desc *desc, const void *
     if (kv_capacity < 0) return FD_ERR_INVALID_ARG;
     if (desc->B == 0) return FD_OK;
     if (!q || !k || !v || !part_o || !part_m || !part_l) return FD_ERR_INVALID_ARG;
+    if (!aligned_io(q, k, v, nullptr, nullptr, seq_lens, fallback_count) ||
+        !aligned_partials(part_o, part_m, part_l))
+        return FD_ERR_INVALID_ARG;
     fd::PartialParams p = base_params(desc);
     p.q = q;
     p.k = k;
@@ -176,6 +194,8 @@ FD_API fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float 
     if (st != FD_OK) return st;
     if (desc->B == 0) return FD_OK;
     if (!part_o || !part_m || !part_l || !out) return FD_ERR_INVALID_ARG;
+    if (!aligned_partials(part_o, part_m, part_l) || !aligned_io(nullptr, nullptr, nullptr, out, lse, seq_lens, nullptr))
+        return FD_ERR_INVALID_ARG;
     return run_combine(desc, part_o, part_m, part_l, seq_lens, out, lse, static_cast<hipStream_t>(stream));
 }
 
@@ -196,7 +216,9 @@ FD_API fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q,
     if ((int64_t)max_blocks_per_seq * page_size > INT32_MAX) return FD_ERR_INVALID_ARG;
     if (desc->B == 0) return FD_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !workspace || !out) return FD_ERR_INVALID_ARG;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256) return FD_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256) || !aligned(block_table, 4) ||
+        !aligned_io(q, k_cache, v_cache, out, lse, seq_lens, fallback_count))
+        return FD_ERR_INVALID_ARG;
     const WorkspaceLayout w = layout(desc);
     if (workspace_bytes < w.total) return FD_ERR_WORKSPACE_TOO_SMALL;
     char *ws = static_cast<char *>(workspace);

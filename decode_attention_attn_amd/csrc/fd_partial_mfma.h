@@ -330,6 +330,16 @@ __device__ __forceinline__ int chunk_slot(int c) {
     return f8_of(T) ? c ^ ((c >> 3) & 1) : c;
 }
 
+// The lanes of one wave exchange data through its private LDS tiles (and the
+// rescale factors): a wavefront-scope fence plus a wave barrier keep every
+// lane's LDS writes ordered before other lanes' reads, and those reads before
+// the next writes.  Both are compiler-only; no s_barrier is emitted.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A block's K and V registers -> the wave's LDS tiles (the registers are
 // free again afterwards).
 template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
@@ -418,6 +428,7 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
         // rescale the P x V accumulators (heads on rows 4 * (l / 16) + r)
         if (__any(moved)) {
             if (lane < 16) sm.corr[wave][lane] = corr;
+            wave_lds_sync();
             const float4 cf = *reinterpret_cast<const float4 *>(&sm.corr[wave][4 * mq]);
 #pragma unroll
             for (int i = 0; i < C::SL; ++i) {
@@ -489,11 +500,13 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
     load_block<T, D>(p, br, t1, off, kr, vr);
     for (int j = 0; j < n; ++j) {
         write_tiles<T, D, GMAX, WAVES, UNIFIED>(kr, vr, sm);
+        wave_lds_sync();
         const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tw + (j + 1) * tstep, t1);
         load_block<T, D>(p, bn, t1, off, kr, vr);
 #pragma unroll
         for (int rt = 0; rt < row_tiles(GMAX); ++rt)
             compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim[rt], qop[rt], st[rt], sm);
+        wave_lds_sync();   // this block's tile reads before the next block's writes
         br = bn;
     }
 }

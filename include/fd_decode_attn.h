@@ -19,8 +19,11 @@
  *    `stream` (a hipStream_t; NULL = the null stream) and returns a status.
  *    Device faults (for instance from a table entry the caller got wrong) show
  *    up at the caller's next synchronisation, not in the status.
- *  - Tensors are dense, row-major, with 16-byte aligned base pointers; offsets
- *    are computed in 64 bits.
+ *  - Tensors are dense and row-major; offsets are computed in 64 bits.  q, K,
+ *    V, part_o and out must be 16-byte aligned (they move 16 bytes at a time;
+ *    the Flash-Decoding page's "Production Implementation Guidelines" ask for
+ *    aligned buffers), every other tensor aligned to its element size;
+ *    a misaligned pointer returns FD_ERR_INVALID_ARG.
  *  - q has shape [B, q_len, Hq, d] ([B, Hq, d] for q_len = 1) and the same
  *    element type as the cache, except with an 8-bit cache, where q is f16 or
  *    bf16 (desc->q_dtype).

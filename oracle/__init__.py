@@ -72,8 +72,27 @@ def lib():
     return _lib
 
 
+def host_cpus() -> dict:
+    """What the host offers this process: every CPU it has (nproc), those the
+    process may run on (its affinity mask), and the OpenMP thread limit the
+    environment sets, if any."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    limit = os.environ.get("OMP_NUM_THREADS", "")
+    return {"nproc": os.cpu_count() or 1, "affinity": affinity,
+            "omp_num_threads": int(limit) if limit.isdigit() and int(limit) > 0 else None}
+
+
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """One thread per CPU the process may run on, within OMP_NUM_THREADS when
+    the environment sets it (a shared host's allotment to this process)."""
+    c = host_cpus()
+    n = c["affinity"]
+    if c["omp_num_threads"]:
+        n = min(n, c["omp_num_threads"])
+    return max(1, n)
 
 
 # ----------------------------------------------------------------------------

@@ -245,3 +245,51 @@ def test_combine_validation():
     desc.d = 32
     assert L.fd_decode_attn_combine(C.byref(desc), None, None, None, None, None, None, None) == \
         fd.FD_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------------------
+# alignment: q, K, V, part_o and out move 16 bytes at a time; the other
+# tensors need their element size.  Each call below hands well-formed fake
+# device addresses with exactly one of them misaligned, so validation must
+# refuse it before anything is launched.
+# ----------------------------------------------------------------------------
+_A = 0x7F0000000000          # a 256-byte aligned stand-in address (never dereferenced)
+
+
+def _addr(i, off=0):
+    return C.c_void_p(_A + i * 0x100000 + off)
+
+
+@pytest.mark.parametrize("pos,off", [(0, 8), (1, 4), (2, 2), (4, 2), (5, 8), (6, 2), (7, 1), (9, 2)])
+def test_partial_rejects_misaligned_pointers(pos, off):
+    """Positions: 0 q, 1 k, 2 v, 4 seq_lens, 5 part_o, 6 part_m, 7 part_l, 9 fallback_count."""
+    L = fd.lib()
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    args = [_addr(i) for i in range(10)]
+    args[3] = C.c_int32(16)
+    args[pos] = _addr(pos, off)
+    assert L.fd_decode_attn_partial(C.byref(desc), *args, None) == fd.FD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("pos,off", [(0, 4), (1, 2), (2, 1), (4, 8), (5, 2)])
+def test_combine_rejects_misaligned_pointers(pos, off):
+    """Positions: 0 part_o, 1 part_m, 2 part_l, 4 out, 5 lse (3 is seq_lens)."""
+    L = fd.lib()
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    args = [_addr(i) for i in range(6)]
+    args[pos] = _addr(pos, off)
+    assert L.fd_decode_attn_combine(C.byref(desc), *args, None) == fd.FD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("pos,off", [(0, 8), (1, 8), (2, 4), (5, 2), (7, 2), (8, 16), (10, 8), (11, 2),
+                                     (13, 2)])
+def test_paged_rejects_misaligned_pointers(pos, off):
+    """Positions: 0 q, 1 k_cache, 2 v_cache, 5 block_table, 7 seq_lens,
+    8 workspace (256 bytes), 10 out, 11 lse, 13 fallback_count."""
+    L = fd.lib()
+    desc = fd.make_desc(2, 8, 8, 128, "bf16", split_size=256, max_splits=4)
+    ws = fd.fd_workspace_bytes(desc)
+    args = [_addr(0), _addr(1), _addr(2), C.c_int32(64), C.c_int32(16), _addr(5), C.c_int32(64), _addr(7),
+            _addr(8), C.c_size_t(ws), _addr(10), _addr(11), _addr(12), _addr(13)]
+    args[pos] = _addr(pos, off)
+    assert L.fd_decode_attn_paged(C.byref(desc), *args, None) == fd.FD_ERR_INVALID_ARG

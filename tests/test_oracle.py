@@ -83,11 +83,23 @@ def test_decode_f16_all_patterns_match_numpy():
     np.testing.assert_array_equal(got, h.astype(np.float64))
 
 
-def test_decode_bf16_all_patterns_match_fp32_widening():
+def test_decode_bf16_all_patterns_match_torch():
+    """Every bfloat16 bit pattern against torch's own bfloat16 -> float64
+    conversion (an implementation independent of the oracle and of synth)."""
+    import torch
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    want = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     got = oracle.decode(bits, "bf16")
-    np.testing.assert_array_equal(got, want)
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    # NaN: exponent all ones, mantissa non-zero (127 patterns per sign)
+    assert int(nan.sum()) == 2 * 127
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    # signed zeros and infinities keep their sign; landmarks of the format
+    assert got[0x0000] == 0.0 and math.copysign(1, got[0x8000]) < 0
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+    assert got[0x3F80] == 1.0 and got[0x4000] == 2.0 and got[0xC040] == -3.0
+    assert got[0x0001] == 2.0 ** -133 and got[0x0080] == 2.0 ** -126
 
 
 def test_decode_e4m3_all_patterns_match_torch_and_the_ocp_table():
