@@ -76,13 +76,14 @@ def lib():
         L.fd_decode_attn_combine.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
         L.fd_decode_attn_paged.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, vp, C.c_size_t, vp, vp, vp,
                                            vp, vp]
+        L.fd_decode_attn_paged_noalloc.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.fd_workspace_bytes.argtypes = [dp]
         L.fd_workspace_bytes.restype = C.c_size_t
         L.fd_split_heuristic.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(i32), C.POINTER(i32)]
         L.fd_status_string.argtypes = [C.c_int]
         L.fd_status_string.restype = C.c_char_p
         for f in ("fd_decode_attn_partial", "fd_decode_attn_combine", "fd_decode_attn_paged",
-                  "fd_split_heuristic"):
+                  "fd_decode_attn_paged_noalloc", "fd_split_heuristic"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -239,6 +240,39 @@ def fd_decode_attn_paged(desc, q, k_cache, v_cache, page_size, block_table, seq_
         _stream(stream),
     ]
     _check("fd_decode_attn_paged", lib().fd_decode_attn_paged(C.byref(desc), *args))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FD_NOALLOC_SCRATCH_BYTES
+
+
+def fd_decode_attn_paged_noalloc(desc, q, k_cache, v_cache, page_size, block_table, seq_lens, out, lse=None,
+                                 flags=None, fallback_count=None, stream=None):
+    """fd_decode_attn_paged without a workspace: the partials live in the
+    library's per-GPU scratch array (no allocation in the call)."""
+    torch = _torch()
+    kvt = _tdtype(desc.kv_dtype)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (page_size, desc.Hkv, desc.d):
+        raise ValueError(f"k_cache must be [num_pages, {page_size}, {desc.Hkv}, {desc.d}]")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must match k_cache")
+    if block_table.dim() != 2 or block_table.shape[0] != desc.B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    nrow = desc.B * query_rows(desc) * desc.max_splits
+    args = [
+        _ptr(q, "q", _qdtype(desc), desc.B * query_rows(desc) * desc.d),
+        _ptr(k_cache, "k_cache", kvt),
+        _ptr(v_cache, "v_cache", kvt),
+        C.c_int32(int(k_cache.shape[0])), C.c_int32(int(page_size)),
+        _ptr(block_table, "block_table", torch.int32, align=4),
+        C.c_int32(int(block_table.shape[1])),
+        _ptr(seq_lens, "seq_lens", torch.int32, desc.B, align=4),
+        _ptr(out, "out", _tdtype(desc.out_dtype), desc.B * query_rows(desc) * desc.d),
+        _ptr(lse, "lse", torch.float32, desc.B * query_rows(desc), optional=True, align=4),
+        _ptr(flags, "flags", torch.uint8, nrow, optional=True, align=1),
+        _ptr(fallback_count, "fallback_count", torch.int32, 1, optional=True, align=4),
+        _stream(stream),
+    ]
+    _check("fd_decode_attn_paged_noalloc", lib().fd_decode_attn_paged_noalloc(C.byref(desc), *args))
 
 
 def alloc_partials(desc, device="cuda"):

@@ -19,7 +19,7 @@ CSRC = PKG / "csrc"
 OBJ = ROOT / "_build"
 LIB = PKG / "libfd_decode_attn.so"
 SOURCES = ["fd_api.hip", "fd_partial_valu.hip", "fd_partial_mfma.hip", "fd_partial_mfma_f16.hip",
-           "fd_partial_mfma_bf16.hip", "fd_partial_mfma_f8f16.hip", "fd_partial_mfma_f8bf16.hip", "fd_combine.hip"]
+           "fd_partial_mfma_bf16.hip", "fd_partial_mfma_f8f16.hip", "fd_partial_mfma_f8bf16.hip", "fd_combine.hip", "fd_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

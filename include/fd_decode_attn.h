@@ -173,6 +173,27 @@ fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q, const 
                                void *out, float *lse, uint8_t *flags, int32_t *fallback_count,
                                void *stream);
 
+/* fd_decode_attn_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, whose role a
+ * file-scope device array of FD_NOALLOC_SCRATCH_BYTES bytes takes, one per GPU,
+ * held until the process ends.  The call itself allocates nothing; its first
+ * call on a device looks up that device's copy of the array.
+ *   Returns FD_ERR_WORKSPACE_TOO_SMALL when fd_workspace_bytes(desc) exceeds
+ *   FD_NOALLOC_SCRATCH_BYTES, FD_ERR_HIP if the array's address cannot be had;
+ *   otherwise exactly what fd_decode_attn_paged returns, with the same results.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from different host threads without
+ * ordering) race and give wrong results; calls ordered on one stream are safe.
+ * The array keeps the last call's partials; nothing in it is read before this
+ * call writes it. */
+#define FD_NOALLOC_SCRATCH_BYTES (64u << 20)
+fd_status fd_decode_attn_paged_noalloc(const fd_decode_desc *desc, const void *q, const void *k_cache,
+                                       const void *v_cache, int32_t num_pages, int32_t page_size,
+                                       const int32_t *block_table, int32_t max_blocks_per_seq,
+                                       const int32_t *seq_lens, void *out, float *lse, uint8_t *flags,
+                                       int32_t *fallback_count, void *stream);
+
 /* Bytes of workspace fd_decode_attn_paged needs for `desc` (0 for an invalid desc). */
 size_t fd_workspace_bytes(const fd_decode_desc *desc);
 
