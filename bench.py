@@ -46,6 +46,7 @@ COMBINE_KERNEL = "combine_kernel"
 KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/fd_partial_valu.hip",
                   "decode_attention_attn_amd/csrc/fd_partial_mfma.h",
                   "decode_attention_attn_amd/csrc/fd_device.h",
+                  "decode_attention_attn_amd/csrc/fd_merge.h",
                   "decode_attention_attn_amd/csrc/fd_combine.hip"]
 
 
@@ -115,8 +116,13 @@ def run_gpu(args, inp, wl):
 
     mode = args.mode
     f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
+    if w.dtype == "fp8" and w.k_scales is not None:
+        f8["k_scales"] = torch.tensor(w.k_scales, dtype=torch.float32, device=dev)
+    if w.dtype == "fp8" and w.v_scales is not None:
+        f8["v_scales"] = torch.tensor(w.v_scales, dtype=torch.float32, device=dev)
     desc = fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, split_size=w.split, max_seq_len=w.N, mode=mode,
-                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel, q_len=w.q_len, **f8)
+                        phi=args.phi, lo=args.lo, hi=args.hi, kernel=args.kernel, q_len=w.q_len, merge=args.merge,
+                        fallback=args.fallback, **f8)
     S = desc.max_splits
     out = torch.empty((w.B, w.q_len * w.Hq, w.d), dtype=fd._tdtype(desc.out_dtype), device=dev)
     lse = torch.empty((w.B, w.q_len * w.Hq), dtype=torch.float32, device=dev)
@@ -130,18 +136,26 @@ def run_gpu(args, inp, wl):
 
     if w.page_size:
         ws = fd.alloc_workspace(desc, dev)
-        n = w.B * w.q_len * w.Hq * S
-        o_b = (n * w.d * 4 + 255) // 256 * 256
-        m_b = (n * 4 + 255) // 256 * 256
-        fw = ws.view(torch.float32)
-        po = fw[:n * w.d]
-        pm = fw[o_b // 4:o_b // 4 + n]
-        pl = fw[(o_b + m_b) // 4:(o_b + m_b) // 4 + n]
-        # the paged entry point does both kernels; time it as partial, report the split in rocprof
+        # the paged entry point does partial and merge; time it as one, the kernels split in rocprof
         calls = []
         for i in range(copies):
             calls.append(lambda i=i: fd.fd_decode_attn_paged(desc, q, ks[i], vs[i], w.page_size, table, lens, ws,
                                                              out, lse, flags, count, stream))
+        combine = None
+    elif args.merge != "separate":
+        # fd_decode_attn: partial and merge in one call (one launch when the merge is fused)
+        ws = fd.alloc_workspace(desc, dev)
+        fd.fd_decode_attn(desc, q, ks[0], vs[0], w.N, lens, ws, out, lse, flags, count, stream)
+        vp = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+        fargs = [(dref, vp(q), vp(ks[i]), vp(vs[i]), C.c_int32(w.N), vp(lens), vp(ws), C.c_size_t(ws.numel()),
+                  vp(out), vp(lse), vp(flags), vp(count), sp) for i in range(copies)]
+        full_fn = L.fd_decode_attn
+
+        def check_full(st):
+            if st != 0:
+                raise RuntimeError(f"fd_decode_attn: {fd.fd_status_string(st)}")
+
+        calls = [lambda i=i: check_full(full_fn(*fargs[i])) for i in range(copies)]
         combine = None
     else:
         po, pm, pl, _ = fd.alloc_partials(desc, dev)
@@ -233,15 +247,22 @@ def run_gpu(args, inp, wl):
 
 def fallback_stats(inp, flags, args):
     """Flagged (request, query head, split) triples of the last step, out of those
-    that hold tokens; each flagged one was recomputed with the synchronized softmax."""
+    that hold tokens; each flagged one was recomputed with the synchronized softmax
+    (with the whole-row fallback: every split of a row with a flagged split)."""
     w = inp.w
     S = flags.shape[-1]
     lens = inp.seq_lens.astype(np.int64)[:, None]
     causal = np.clip(lens - w.q_len + np.arange(w.q_len)[None, :] + 1, 0, lens)   # tokens each query row sees
-    valid = int(np.minimum(-(-causal // w.split), S).sum()) * w.Hq
+    per_row = np.repeat(np.minimum(-(-causal // w.split), S).reshape(-1), w.Hq)   # splits with tokens, by row
+    valid = int(per_row.sum())
     n = int(flags.astype(np.int64).sum())
-    return {"flagged_splits": n, "splits_with_tokens": valid, "rate": n / max(valid, 1),
-            "phi": args.phi, "lo": args.lo, "hi": args.hi}
+    rows_flagged = flags.reshape(-1, S).astype(bool).any(axis=1)
+    out = {"flagged_splits": n, "splits_with_tokens": valid, "rate": n / max(valid, 1), "fallback": args.fallback,
+           "phi": args.phi, "lo": args.lo, "hi": args.hi}
+    if args.fallback == "row":
+        out["rows_flagged"] = int(rows_flagged.sum())
+        out["recomputed_splits"] = int(per_row[rows_flagged].sum())
+    return out
 
 
 def parity_spot_check(inp, res, rows):
@@ -311,22 +332,45 @@ def cpu_baseline(inp, alg, seconds):
 def run_settings(args):
     """The bench options that select which kernel runs and how."""
     s = {"kernel": args.kernel, "mode": args.mode}
+    if args.merge != "separate":
+        s["merge"] = args.merge
     if args.mode == "unified":
         s.update(phi=args.phi, lo=args.lo, hi=args.hi)
+        if args.fallback != "split":
+            s["fallback"] = args.fallback
     return s
 
 
-def traffic_from_profile(workload, kernel_name, settings):
-    """HBM bytes per launch of the partial kernel from the committed PMC summary,
-    if it was taken with the same kernel sources and run settings; else None."""
+def kernel_key(name):
+    """Key of a kernel in the PMC summaries: the single-launch kernel, a
+    split-partial kernel, the combine, or the name itself."""
+    if "fused_mfma_kernel" in name:
+        return "fused"
+    if "partial" in name:
+        return PARTIAL_KERNEL
+    if "combine" in name:
+        return "combine"
+    return name[:60]
+
+
+def traffic_from_profile(workload, kernel_keys, settings):
+    """HBM bytes per timed call (the sum over `kernel_keys`, one launch each)
+    from the committed PMC summary, if it was taken with the same kernel
+    sources and run settings; else None.  kernel_keys may also be a list of
+    such lists (the kernels a call may have launched): the first one the
+    summary holds in full is used."""
     f = ROOT / "profiles" / f"{workload}_pmc.json"
     if not f.exists():
         return None
     d = json.loads(f.read_text())
     if d.get("source_hash") != source_hash() or d.get("settings") != settings:
         return None
-    k = d.get("kernels", {}).get(kernel_name)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    options = kernel_keys if kernel_keys and isinstance(kernel_keys[0], list) else [kernel_keys]
+    kernels = d.get("kernels", {})
+    for keys in options:
+        if all(k in kernels for k in keys):
+            return sum(kernels[k]["hbm_bytes_per_launch"] for k in keys)
+    return None
 
 
 def main():
@@ -340,6 +384,13 @@ def main():
     ap.add_argument("--lo", type=float, default=-20.0)
     ap.add_argument("--hi", type=float, default=20.0)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--fallback", default="split", choices=["split", "row"],
+                    help="unified max: recompute the flagged split, or every split of a flagged row")
+    ap.add_argument("--merge", default=None, choices=["separate", "fused", "auto"],
+                    help="separate: a contiguous cache through the partial and combine entry points (two "
+                         "launches, timed one by one); fused / auto: fd_decode_attn (or the paged entry point) "
+                         "with that merge mode.  Default: separate for a contiguous cache (what auto picks for "
+                         "the contiguous workloads), auto for a paged one")
     ap.add_argument("--split", type=int, default=0,
                     help="split size override (default: the workload's; a sweep knob, not the headline)")
     ap.add_argument("--warm", action="store_true", help="one KV copy (cache-resident for small caches)")
@@ -354,6 +405,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE runs into profiles/<workload>_pmc.json")
     args = ap.parse_args()
+    if args.merge is None:
+        import synth
+        args.merge = "auto" if synth.WORKLOADS[args.workload].page_size else "separate"
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
@@ -380,8 +434,18 @@ def main():
     parity = parity_spot_check(inp, g["res"], np.arange(0, w.B * w.q_len * w.Hq, max(1, (w.B * w.q_len * w.Hq) // 32)))
     log(f"[bench] step {g['step_ms'] * 1e3:.2f} us, partial {np.mean(g['part_us']):.2f} us, "
         f"combine {np.mean(g['comb_us']):.2f} us (back-to-back averages); parity {parity}")
-    kname = "fd_decode_attn_paged" if w.page_size else PARTIAL_KERNEL
-    traffic = traffic_from_profile(w.name, kname, run_settings(args))
+    kname = "fd_decode_attn_paged" if w.page_size else ("fd_decode_attn" if args.merge != "separate" else PARTIAL_KERNEL)
+    # the kernels one timed call launches: the entry points with a merge run the
+    # partial and the combine, or the single fused kernel
+    if kname == PARTIAL_KERNEL:
+        keys = [PARTIAL_KERNEL]
+    elif args.merge == "fused":
+        keys = ["fused"]
+    elif args.merge == "separate":
+        keys = [PARTIAL_KERNEL, "combine"]
+    else:   # auto: whichever the library took
+        keys = [["fused"], [PARTIAL_KERNEL, "combine"]]
+    traffic = traffic_from_profile(w.name, keys, run_settings(args))
     achieved = alg["partial"] / part_s / 1e9
     line = {
         "metric": "decode-attn us/step and achieved HBM TB/s (% of MI355X peak), N=32k GQA",
@@ -400,7 +464,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": w.N, "q_len": w.q_len,
                    "kv_dtype": w.dtype, "split": w.split, "num_splits": g["S"], "page_size": w.page_size,
-                   "softmax": args.mode, "kernel": args.kernel, "kv_copies": g["copies"],
+                   "softmax": args.mode, "kernel": args.kernel, "merge": args.merge, "kv_copies": g["copies"],
                    "launch": "hip graph" if args.graph else "eager",
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
         "kernels_us": {"partial": float(np.mean(g["part_us"])), "combine": float(np.mean(g["comb_us"])),
@@ -504,7 +568,7 @@ def pmc_summary(workload, fetch_dir, write_dir, settings):
         fk = fetch.get(name, (0, 0.0))
         wk = write.get(name, (0, 0.0))
         hbm = fk[1] * 1024 * f_scale + wk[1] * 1024 * w_scale
-        key = PARTIAL_KERNEL if "partial" in name else ("combine" if "combine" in name else name[:60])
+        key = kernel_key(name)
         out["kernels"][key] = {"name": name, "fetch_kib": fk[1], "write_kib": wk[1], "hbm_bytes_per_launch": hbm,
                                "dispatches": max(fk[0], wk[0])}
         short = name if len(name) < 80 else name[:77] + "..."

@@ -12,6 +12,8 @@
 
 #define FD_API extern "C" __attribute__((visibility("default")))
 
+static_assert(FD_TICKET_BYTES == fd::kTicketBytes, "the header's ticket area is the library's");
+
 namespace {
 
 using fd::kMaxGroup;
@@ -48,6 +50,11 @@ fd_status validate_desc(const fd_decode_desc *d) {
             return FD_ERR_INVALID_ARG;
     }
     if (d->kernel < FD_KERNEL_AUTO || d->kernel > FD_KERNEL_MFMA) return FD_ERR_INVALID_ARG;
+    if (d->merge < FD_MERGE_AUTO || d->merge > FD_MERGE_FUSED) return FD_ERR_INVALID_ARG;
+    if (d->fallback < FD_FALLBACK_SPLIT || d->fallback > FD_FALLBACK_ROW) return FD_ERR_INVALID_ARG;
+    if (d->kv_dtype == FD_FP8_E4M3 &&
+        ((reinterpret_cast<uintptr_t>(d->k_scales) & 3) || (reinterpret_cast<uintptr_t>(d->v_scales) & 3)))
+        return FD_ERR_INVALID_ARG;
     return FD_OK;
 }
 
@@ -84,8 +91,12 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     p.v_mult = 1.f;
     if (d->kv_dtype == FD_FP8_E4M3) {   // stored K / V values stand for stored * scale
         p.q_dtype = d->q_dtype;
-        scale *= d->k_scale > 0.f ? (double)d->k_scale : 1.0;
-        p.v_mult = d->v_scale > 0.f ? d->v_scale : 1.f;
+        // per-KV-head scales replace the per-tensor ones; the kernels multiply
+        // the score scale and V by the head's entry
+        p.k_scales = d->k_scales;
+        p.v_scales = d->v_scales;
+        if (!d->k_scales) scale *= d->k_scale > 0.f ? (double)d->k_scale : 1.0;
+        if (!d->v_scales) p.v_mult = d->v_scale > 0.f ? d->v_scale : 1.f;
     }
     const double log2e = 1.4426950408889634;
     p.scale_log2 = (float)(scale * log2e);
@@ -98,8 +109,9 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     return p;
 }
 
-fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t stream) {
-    bool mfma = false;
+// Which partial kernel runs: MFMA or VALU (FD_ERR_UNSUPPORTED if the one asked for cannot).
+fd_status pick_kernel(const fd_decode_desc *d, const fd::PartialParams &p, bool &mfma) {
+    mfma = false;
     if (d->kernel == FD_KERNEL_MFMA) {
         if (!fd::mfma_supports(p)) return FD_ERR_UNSUPPORTED;
         mfma = true;
@@ -107,8 +119,74 @@ fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t
         mfma = fd::mfma_supports(p);
     }
     if (!mfma && p.R > kMaxGroup) return FD_ERR_UNSUPPORTED;   // the VALU kernel holds up to 16 rows
-    const hipError_t e = mfma ? fd::launch_partial_mfma(p, stream) : fd::launch_partial_valu(p, stream);
+    return FD_OK;
+}
+
+bool whole_row_fallback(const fd_decode_desc *d) {
+    return d->mode == FD_SOFTMAX_UNIFIED_MAX && d->fallback == FD_FALLBACK_ROW;
+}
+
+// The split partials.  With the whole-row fallback: the unified pass writes
+// every row's partials and the flags, then a synchronized pass rewrites all
+// splits of every row that has a flagged split (its workgroups read the
+// flags and leave at once where no row of theirs is flagged).
+fd_status run_partial(const fd_decode_desc *d, fd::PartialParams &p, hipStream_t stream) {
+    bool mfma = false;
+    const fd_status st = pick_kernel(d, p, mfma);
+    if (st != FD_OK) return st;
+    const bool rows = whole_row_fallback(d);
+    if (rows && !p.flags) return FD_ERR_INVALID_ARG;   // the second pass reads the flags
+    p.row_fallback = rows;
+    auto launch = [&](const fd::PartialParams &q) {
+        return mfma ? fd::launch_partial_mfma(q, stream) : fd::launch_partial_valu(q, stream);
+    };
+    hipError_t e = launch(p);
+    if (e == hipSuccess && rows) {
+        fd::PartialParams r = p;
+        r.unified = 0;
+        r.row_fallback = 0;
+        r.recompute_rows = 1;
+        r.fallback_count = nullptr;
+        e = launch(r);
+    }
     return e == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+// Splits per workgroup of the single-launch MFMA kernel: four waves' worth
+// of splits, so that the merging workgroup has 256 threads and a head's
+// workgroup partials stay few (two for short requests).
+int fused_splits_per_wg(const fd::PartialParams &p) { return p.max_splits >= 8 ? 4 : 2; }
+
+// Whether the single-launch merge can run this shape: the counters fit the
+// workspace's ticket area, one request's partials span less than 4 GiB (the
+// merge addresses them with 32-bit offsets), and one workgroup's merge fits
+// its LDS.
+bool fused_fits(const fd::PartialParams &p, bool mfma) {
+    if ((int64_t)p.B * p.Hkv > fd::kMaxTickets) return false;
+    if ((int64_t)p.q_len * p.Hq * p.max_splits * p.d * 4 >= ((int64_t)1 << 32)) return false;
+    const int64_t parts = mfma ? (p.max_splits + p.splits_per_wg - 1) / p.splits_per_wg : p.max_splits;
+    return (int64_t)p.R * parts <= fd::kFusedMaxRowParts;
+}
+
+// The single launch where it is asked for, and under FD_MERGE_AUTO where it
+// was measured to win: it saves the second launch and the re-read of the
+// partials, which pays when the partials are many, and costs its
+// four-wave workgroups and the tail of the last merges otherwise.  Measured
+// on MI355X (bench.py --merge fused / separate, two runs each): B=64 ragged
+// paged batch at split 256, 128 MiB of partial rows: 458 against 488 us per
+// call; B=4, N=128k at split 1024, 16 MiB: 368 against 361 us; 32k GQA,
+// 2 MiB: 29.6 against 29.1-29.3 us; Llama-2-shaped MHA, 256 KiB: 20.7
+// against 18.3-18.9 us.
+bool fused_wanted(const fd_decode_desc *d, const fd::PartialParams &p, bool mfma) {
+    (void)mfma;
+    if (d->merge != FD_MERGE_AUTO) return d->merge == FD_MERGE_FUSED;
+    const double partial_bytes = (double)p.B * p.q_len * p.Hq * p.max_splits * p.d * sizeof(float);
+    return partial_bytes >= 64.0 * (1 << 20);
+}
+
+// The single launch has no room for the whole-row fallback's second pass.
+bool fused_possible(const fd_decode_desc *d, const fd::PartialParams &p, bool mfma) {
+    return !whole_row_fallback(d) && fused_fits(p, mfma);
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -128,16 +206,19 @@ bool aligned_io(const void *q, const void *k, const void *v, const void *out, co
            aligned(seq_lens, 4) && aligned(fallback_count, 4);
 }
 
+// Workspace: the single-launch merge's counters (fd::kTicketBytes), then
+// part_o, part_m and part_l, each on a 256-byte boundary.
 struct WorkspaceLayout {
-    size_t o_bytes, m_bytes, total;
+    size_t o_off, m_off, l_off, total;
 };
 
 WorkspaceLayout layout(const fd_decode_desc *d) {
     const size_t rows = (size_t)d->B * (d->q_len > 1 ? d->q_len : 1) * d->Hq * d->max_splits;
     WorkspaceLayout w;
-    w.o_bytes = round256(rows * d->d * sizeof(float));
-    w.m_bytes = round256(rows * sizeof(float));
-    w.total = w.o_bytes + 2 * w.m_bytes;
+    w.o_off = fd::kTicketBytes;
+    w.m_off = w.o_off + round256(rows * d->d * sizeof(float));
+    w.l_off = w.m_off + round256(rows * sizeof(float));
+    w.total = w.l_off + round256(rows * sizeof(float));
     return w;
 }
 
@@ -204,6 +285,56 @@ FD_API size_t fd_workspace_bytes(const fd_decode_desc *desc) {
     return layout(desc).total;
 }
 
+// Partial + merge over the caller's workspace, for both cache layouts:
+// a separate combine launch, or the single launch with the merge inside.
+fd_status run_full(const fd_decode_desc *desc, fd::PartialParams &p, void *workspace, size_t workspace_bytes,
+                   const int32_t *seq_lens, void *out, float *lse, hipStream_t s) {
+    if (!aligned(workspace, 256)) return FD_ERR_INVALID_ARG;
+    const WorkspaceLayout w = layout(desc);
+    if (workspace_bytes < w.total) return FD_ERR_WORKSPACE_TOO_SMALL;
+    char *ws = static_cast<char *>(workspace);
+    p.part_o = reinterpret_cast<float *>(ws + w.o_off);
+    p.part_m = reinterpret_cast<float *>(ws + w.m_off);
+    p.part_l = reinterpret_cast<float *>(ws + w.l_off);
+    bool mfma = false;
+    fd_status st = pick_kernel(desc, p, mfma);
+    if (st != FD_OK) return st;
+    p.splits_per_wg = fused_splits_per_wg(p);
+    const bool fits = fused_possible(desc, p, mfma);
+    if (desc->merge == FD_MERGE_FUSED && !fits) return FD_ERR_UNSUPPORTED;
+    if (fits && fused_wanted(desc, p, mfma)) {
+        p.tickets = reinterpret_cast<int32_t *>(ws);
+        p.out = out;
+        p.lse = lse;
+        p.out_dtype = desc->out_dtype;
+        const hipError_t e = mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, s);
+        return e == hipSuccess ? FD_OK : FD_ERR_HIP;
+    }
+    st = run_partial(desc, p, s);
+    if (st != FD_OK) return st;
+    return run_combine(desc, p.part_o, p.part_m, p.part_l, seq_lens, out, lse, s);
+}
+
+FD_API fd_status fd_decode_attn(const fd_decode_desc *desc, const void *q, const void *k, const void *v,
+                                int32_t kv_capacity, const int32_t *seq_lens, void *workspace, size_t workspace_bytes,
+                                void *out, float *lse, uint8_t *flags, int32_t *fallback_count, void *stream) {
+    fd_status st = validate_desc(desc);
+    if (st != FD_OK) return st;
+    if (kv_capacity < 0) return FD_ERR_INVALID_ARG;
+    if (desc->B == 0) return FD_OK;
+    if (!q || !k || !v || !workspace || !out) return FD_ERR_INVALID_ARG;
+    if (!aligned_io(q, k, v, out, lse, seq_lens, fallback_count)) return FD_ERR_INVALID_ARG;
+    fd::PartialParams p = base_params(desc);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.seq_lens = seq_lens;
+    p.kv_capacity = kv_capacity;
+    p.flags = flags;
+    p.fallback_count = fallback_count;
+    return run_full(desc, p, workspace, workspace_bytes, seq_lens, out, lse, static_cast<hipStream_t>(stream));
+}
+
 FD_API fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q, const void *k_cache,
                                       const void *v_cache, int32_t num_pages, int32_t page_size,
                                       const int32_t *block_table, int32_t max_blocks_per_seq,
@@ -219,13 +350,6 @@ FD_API fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q,
     if (!aligned(workspace, 256) || !aligned(block_table, 4) ||
         !aligned_io(q, k_cache, v_cache, out, lse, seq_lens, fallback_count))
         return FD_ERR_INVALID_ARG;
-    const WorkspaceLayout w = layout(desc);
-    if (workspace_bytes < w.total) return FD_ERR_WORKSPACE_TOO_SMALL;
-    char *ws = static_cast<char *>(workspace);
-    float *part_o = reinterpret_cast<float *>(ws);
-    float *part_m = reinterpret_cast<float *>(ws + w.o_bytes);
-    float *part_l = reinterpret_cast<float *>(ws + w.o_bytes + w.m_bytes);
-
     fd::PartialParams p = base_params(desc);
     p.q = q;
     p.k = k_cache;
@@ -236,15 +360,9 @@ FD_API fd_status fd_decode_attn_paged(const fd_decode_desc *desc, const void *q,
     p.max_blocks = max_blocks_per_seq;
     p.num_pages = num_pages;
     p.kv_capacity = max_blocks_per_seq * page_size;
-    p.part_o = part_o;
-    p.part_m = part_m;
-    p.part_l = part_l;
     p.flags = flags;
     p.fallback_count = fallback_count;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_partial(desc, p, s);
-    if (st != FD_OK) return st;
-    return run_combine(desc, part_o, part_m, part_l, seq_lens, out, lse, s);
+    return run_full(desc, p, workspace, workspace_bytes, seq_lens, out, lse, static_cast<hipStream_t>(stream));
 }
 
 FD_API fd_status fd_split_heuristic(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t page_size,

@@ -193,6 +193,23 @@ __device__ __forceinline__ int row_limit(const PartialParams &p, int len, int t1
     return lim < t1 ? lim : t1;
 }
 
+// Whole-row fallback, second pass: the query rows (bit rho) of KV head kvh
+// of request b with a flagged split among the request's first nsplit splits.
+// Every lane of the wave reads a share of the flags; the result is
+// wave-uniform.
+__device__ __forceinline__ uint32_t rows_flagged_in_request(const PartialParams &p, int b, int kvh, int nsplit) {
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    for (int idx = lane; idx < p.R * nsplit; idx += 64) {
+        const int rho = idx / nsplit, s = idx - rho * nsplit;
+        const size_t slot = (((size_t)b * p.q_len + rho / p.G) * p.Hq + (size_t)kvh * p.G + rho % p.G) * p.max_splits + s;
+        if (p.flags[slot]) m |= 1u << rho;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m |= (uint32_t)__shfl_xor((int)m, off);
+    return m;
+}
+
 // Number of tokens of request b that the kernels read.
 __device__ __forceinline__ int request_len(const int32_t *seq_lens, int b, int cap, int limit) {
     int n = seq_lens ? seq_lens[b] : cap;

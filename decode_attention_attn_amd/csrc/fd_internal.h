@@ -13,6 +13,11 @@ constexpr int kMaxGroup = 16;       // query heads per KV head
 constexpr int kMaxRows = 32;        // query rows per KV head, q_len * G (MFMA kernel; VALU: 16)
 constexpr int kMaxSplits = 4096;    // the combine stages m and l of every split in LDS
 constexpr int kMaxSplitSize = 1 << 20;
+// single-launch merge: query rows x partials that one workgroup merges
+constexpr int kFusedMaxRowParts = 2048;
+// single-launch merge: (request, KV head) counters at the start of the workspace
+constexpr int kMaxTickets = 65536;
+constexpr size_t kTicketBytes = kMaxTickets * sizeof(int32_t);
 // unified max: |lo - phi|, |hi - phi| bound, so exp(s - phi) <= e^64 leaves
 // fp32 headroom for sums of up to 2^20 terms times |v|
 constexpr float kMaxUnifiedRange = 64.f;
@@ -46,7 +51,21 @@ struct PartialParams {
     int32_t dtype;              // DType of k and v (and of q unless FP8)
     int32_t q_dtype;            // DType of q (F16 or BF16 when dtype is FP8)
     float v_mult;               // FP8: value of one stored V unit (v_scale); else 1
+    const float *k_scales;      // FP8: per-KV-head K scales [Hkv] or nullptr (then scale_log2 holds k_scale)
+    const float *v_scales;      // FP8: per-KV-head V scales [Hkv] or nullptr (then v_mult)
     int32_t num_cus;            // compute units of the device (launch-shape choice only)
+    // single-launch merge (tickets != nullptr): one counter per (request, KV
+    // head), zero on entry and left zero; the merged result goes to out / lse
+    int32_t *tickets;
+    void *out;                  // [B, q_len * Hq, d] of out_dtype
+    float *lse;                 // [B, q_len * Hq] or nullptr
+    int32_t out_dtype;
+    int32_t splits_per_wg;      // MFMA kernel: consecutive splits per workgroup (2 or 4)
+    // whole-row fallback of unified max: the unified pass writes every row's
+    // partial and only flags (row_fallback); a second, synchronized pass
+    // (recompute_rows) rewrites every split of the rows flagged anywhere
+    int32_t row_fallback;
+    int32_t recompute_rows;
 };
 
 struct CombineParams {

@@ -42,7 +42,10 @@
 // written as one split partial.
 #pragma once
 
+#include <type_traits>
+
 #include "fd_device.h"
+#include "fd_merge.h"
 
 namespace fd {
 namespace {
@@ -102,6 +105,13 @@ __device__ __forceinline__ void split_probs(const float (&pr)[4], s16x4 &hi, s16
 }
 
 constexpr int kBlk = 16;   // tokens per MFMA block
+
+// The wave of this thread among the WAVES waves that share one split (a
+// kernel whose waves each scan a split of their own passes WAVES = 1).
+template <int WAVES>
+__device__ __forceinline__ int head_wave() {
+    return WAVES == 1 ? 0 : (int)(threadIdx.x >> 6) % WAVES;
+}
 
 // Register budget and the order of the P x V operand reads, by query rows
 // per KV head (measured on MI355X, each A/B in one session).  Up to four
@@ -163,7 +173,8 @@ struct MSmem {
     };
     union {
         uint4 k[WAVES][kBlk * C::ROWB / 16];      // wave-private K tiles ...
-        Handover ho;                              // ... reused by the epilogue once both waves are done
+        // ... reused by the epilogue once both waves of a head are done (one wave: no hand-over)
+        typename std::conditional<(WAVES > 1), Handover, char>::type ho;
     };
     uint4 v[WAVES][kBlk * C::ROWB / 16];          // wave-private V tiles
     float corr[WAVES][16];                        // running-max rescale factors per head row
@@ -348,7 +359,7 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
     using C = MCfg<D, GMAX, WAVES>;
     using L = KLoad<T, D>;
     constexpr int DT = op_of(T);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = head_wave<WAVES>();
     const int rg = lane / L::LPR, ch = lane % L::LPR;
     char *ktile = reinterpret_cast<char *>(sm.k[wave]);
     char *vtile = reinterpret_cast<char *>(sm.v[wave]);
@@ -375,14 +386,16 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
 }
 
 // One block from the wave's tiles into the running state.
-// lim: this lane's query row (lane % 16) sees tokens < lim of the split
+// lim: this lane's query row (lane % 16) sees tokens < lim of the split;
+// sc: the score scale in log2 units (scale * log2(e), times the KV head's K
+// scale for 8-bit caches)
 template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void compute_tiles(const PartialParams &p, const BlockRows &br, int lim,
+__device__ __forceinline__ void compute_tiles(const PartialParams &p, const BlockRows &br, int lim, float sc,
                                               const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
                                               MSmem<D, GMAX, WAVES> &sm) {
     using C = MCfg<D, GMAX, WAVES>;
     constexpr int DT = op_of(T);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = head_wave<WAVES>();
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
     const char *ktile = reinterpret_cast<const char *>(sm.k[wave]);
     const char *vtile = reinterpret_cast<const char *>(sm.v[wave]);
@@ -399,7 +412,7 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const bool ok = br.page_ok && br.tb + 4 * mq + r < lim;
-        s[r] = ok ? acc[r] * p.scale_log2 : -INFINITY;
+        s[r] = ok ? acc[r] * sc : -INFINITY;
     }
 
     // ---- softmax for head mrow over these 16 tokens
@@ -480,11 +493,11 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
 // block's page from them with a lane read.  Each block runs through the
 // matrix work once per 16-row tile of query rows.
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1,
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, float sc,
                            const int (&lim)[row_tiles(GMAX)], const uint4 (&qop)[row_tiles(GMAX)][D / 32],
                            MState<D, GMAX> (&st)[row_tiles(GMAX)], MSmem<D, GMAX, WAVES> &sm) {
     using L = KLoad<T, D>;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(head_wave<WAVES>());
     const auto off = lane_offsets<T, D>(p);
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
     const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
@@ -505,7 +518,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
         load_block<T, D>(p, bn, t1, off, kr, vr);
 #pragma unroll
         for (int rt = 0; rt < row_tiles(GMAX); ++rt)
-            compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim[rt], qop[rt], st[rt], sm);
+            compute_tiles<T, D, GMAX, WAVES, UNIFIED>(p, br, lim[rt], sc, qop[rt], st[rt], sm);
         wave_lds_sync();   // this block's tile reads before the next block's writes
         br = bn;
     }
@@ -515,10 +528,10 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 // for the rows in write_mask.
 template <int T, int D, int GMAX, int WAVES>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
-                             int s, uint32_t write_mask, int rt) {
+                             int s, uint32_t write_mask, int rt, float vmul) {
     using C = MCfg<D, GMAX, WAVES>;
     constexpr int GQ = MSmem<D, GMAX, WAVES>::GQ < 4 ? MSmem<D, GMAX, WAVES>::GQ : 4;   // head quads per tile
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = head_wave<WAVES>();
     const int mrow = lane & 15, mq = lane >> 4;
     // wave 0 writes the partial straight from its registers: lane
     // (mrow, mq) holds dim 16 * slice + mrow of rows 4 * mq + r, and reads
@@ -565,7 +578,7 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
         if (g >= p.R || !((write_mask >> g) & 1u)) continue;
         const size_t slot = row_slot(p, b, kvh, g, s);
         float inv = L > 0.f ? 1.f / L : 0.f;
-        if constexpr (f8_of(T)) inv *= p.v_mult;   // a stored V unit stands for v_scale
+        if constexpr (f8_of(T)) inv *= vmul;   // a stored V unit stands for the head's V scale
 #pragma unroll
         for (int i = 0; i < C::SL; ++i) {
             float a = st.o[i][r];
@@ -601,6 +614,51 @@ __device__ __forceinline__ int kv_head_of(const PartialParams &p, int y) {
     return y < half ? 2 * y + 1 : 2 * (y - half);
 }
 
+// The B operand of each 16-row tile (q of query row 16 rt + lane % 16, dims
+// 8 * (lane / 16) of each 32-dim step; rows >= R zero) and each lane's causal
+// limit within the split ending at t1.
+template <int D, int GMAX>
+__device__ __forceinline__ void load_q_operand(const PartialParams &p, int b, int kvh, int len, int t1,
+                                               uint4 (&qop)[row_tiles(GMAX)][D / 32], int (&lim)[row_tiles(GMAX)]) {
+    const int lane = threadIdx.x & 63, R = p.R;
+#pragma unroll
+    for (int rt = 0; rt < row_tiles(GMAX); ++rt) {
+        const int rho = 16 * rt + (lane & 15);
+        lim[rt] = row_limit(p, len, t1, rho);
+        const char *qb = static_cast<const char *>(p.q);
+        const size_t qrow = rho < R ? query_row(p, b, kvh, rho) : 0;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            qop[rt][ks] = make_uint4(0, 0, 0, 0);
+            if (rho < R) qop[rt][ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
+        }
+    }
+}
+
+// Query rows of the wave whose scores left [lo, hi] (bit 16 rt + row).
+template <int GMAX, int D>
+__device__ __forceinline__ uint32_t flagged_rows(const MState<D, GMAX> (&st)[row_tiles(GMAX)]) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int rt = 0; rt < row_tiles(GMAX); ++rt) {
+        const uint64_t bal = __ballot(st[rt].bad);
+        mine |= (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu) << (16 * rt);
+    }
+    return mine;
+}
+
+// Score scale (log2 units) and V multiplier of KV head kvh: 8-bit caches fold
+// the head's K scale into the score scale and apply its V scale to O.
+template <int T>
+__device__ __forceinline__ void head_scales(const PartialParams &p, int kvh, float &sc, float &vmul) {
+    sc = p.scale_log2;
+    vmul = p.v_mult;
+    if constexpr (f8_of(T)) {
+        if (p.k_scales) sc *= p.k_scales[kvh];
+        if (p.v_scales) vmul = p.v_scales[kvh];
+    }
+}
+
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
 partial_mfma_kernel(const PartialParams p) {
@@ -616,7 +674,7 @@ partial_mfma_kernel(const PartialParams p) {
     const int t1 = min(t0 + p.split, len);
 
     if (t0 >= t1) {
-        if (threadIdx.x < R) {
+        if (threadIdx.x < R && !p.recompute_rows) {
             const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
             p.part_m[slot] = -INFINITY;
             p.part_l[slot] = 0.f;
@@ -624,25 +682,22 @@ partial_mfma_kernel(const PartialParams p) {
         }
         return;
     }
+    // whole-row fallback, second pass: only rows flagged in some split of the request
+    uint32_t rows_to_write = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
+    if (!UNI && p.recompute_rows) {
+        rows_to_write = rows_flagged_in_request(p, b, kvh, (len + p.split - 1) / p.split);
+        if (!rows_to_write) return;
+    }
 
     constexpr int NT = row_tiles(GMAX);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float sc, vmul;
+    head_scales<T>(p, kvh, sc, vmul);
     // B operand of tile rt: q of query row 16 rt + lane % 16, dims 8 * (lane / 16)
     // of each step; lim[rt]: that row's causal limit
     uint4 qop[NT][C::KS];
     int lim[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-        const int rho = 16 * rt + (lane & 15);
-        lim[rt] = row_limit(p, len, t1, rho);
-        const char *qb = static_cast<const char *>(p.q);
-        const size_t qrow = rho < R ? query_row(p, b, kvh, rho) : 0;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            qop[rt][ks] = make_uint4(0, 0, 0, 0);
-            if (rho < R) qop[rt][ks] = load16(qb + (qrow * D + 32 * ks + 8 * (lane >> 4)) * 2);
-        }
-    }
+    load_q_operand<D, GMAX>(p, b, kvh, len, t1, qop, lim);
 
     const uint32_t all = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
     MState<D, GMAX> st[NT];
@@ -650,38 +705,216 @@ partial_mfma_kernel(const PartialParams p) {
     if constexpr (UNI) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) st[rt].init(p.phi2);
-        scan_split<T, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, lim, qop, st, sm);
-        uint32_t mine = 0;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            const uint64_t bal = __ballot(st[rt].bad);
-            mine |= (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu) << (16 * rt);
-        }
-        if (lane == 0) sm.bad[wave] = mine;
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
-        badmask &= all;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, all & ~badmask, rt);
-        if (badmask) {   // synchronized recompute of the flagged heads
+        scan_split<T, D, GMAX, WAVES, PAGED, true>(p, b, kvh, t0, t1, sc, lim, qop, st, sm);
+        const uint32_t mine = flagged_rows<GMAX>(st);
+        if constexpr (WAVES == 1) {
+            badmask = mine;                          // wave-uniform: the one wave
+        } else {
+            if (lane == 0) sm.bad[wave] = mine;
             __syncthreads();
 #pragma unroll
-            for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
-            scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+            for (int w = 0; w < WAVES; ++w) badmask |= sm.bad[w];
+        }
+        badmask &= all;
+        // whole-row fallback: every row's unified partial now, the flagged rows'
+        // splits all rewritten by a second pass
+        const uint32_t keep = p.row_fallback ? all : all & ~badmask;
 #pragma unroll
-            for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, badmask, rt);
+        for (int rt = 0; rt < NT; ++rt)
+            finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, keep, rt, vmul);
+        if (badmask && !p.row_fallback) {   // synchronized recompute of the flagged heads
+            if constexpr (WAVES > 1) __syncthreads();   // the hand-over area overlays the K tiles
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
+            scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, badmask, rt, vmul);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
-        scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, lim, qop, st, sm);
+        scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm);
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, all, rt);
+        for (int rt = 0; rt < NT; ++rt)
+            finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, rows_to_write, rt, vmul);
     }
-    if (p.flags && threadIdx.x < R) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
+    if (p.flags && threadIdx.x < R && !p.recompute_rows)
+        p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
+}
+
+// ---------------------------------------------------------------------------
+// single launch: partials and their merge in one kernel
+// ---------------------------------------------------------------------------
+// A workgroup covers SW consecutive splits of one (request, KV head), one
+// wave per split, each wave scanning its split exactly as above.  The waves'
+// split states are merged in the workgroup (max-rescale, in split order) into
+// one partial of the SW splits, written with device-scope stores to slot x of
+// the head's partial rows; the last workgroup of the head to finish merges
+// the head's workgroup partials into out and lse (fd_merge.h).  The merge is
+// the same log-sum-exp merge as the separate combine, taken as a two-level
+// tree (splits within a workgroup, then workgroups), which the merge's
+// associativity makes exact (Flash-Decoding page, "The Rescaling and Online
+// Softmax Reduction Algorithm").  Under unified max a wave whose split holds
+// an out-of-range score rescans the split with the synchronized softmax and
+// carries that state for every row of the split.
+template <int D, int GMAX, int SW>
+struct FSmem {
+    static constexpr int NT = row_tiles(GMAX);
+    struct Hand {                                       // one wave's state, lane for lane
+        float4 o[D / 16][64];
+        float l[16], m[16];
+    };
+    union {
+        MSmem<D, GMAX, 1> tiles[SW];                    // each wave's K / V tiles
+        Hand ho[SW > 1 ? SW - 1 : 1][NT];               // waves 1 .. SW-1 hand over to wave 0
+        float merge[merge_lds_floats(kFusedMaxRowParts, kMaxRows, 64 * SW)];   // the last workgroup's merge
+    };
+    int ticket;
+};
+
+// Wave 0: merge the handed-over states of waves 1 .. SW-1 into its own (row
+// tile rt) and write the workgroup's partial to slot x, device scope.
+template <int T, int D, int GMAX, int SW>
+__device__ void store_group_partial(const PartialParams &p, const MState<D, GMAX> &st, float lsum,
+                                    const FSmem<D, GMAX, SW> &sm, int rt, int b, int kvh, int x, float vmul) {
+    constexpr int SL = D / 16;
+    const int lane = threadIdx.x & 63, mrow = lane & 15, mq = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int gl = 4 * mq + r, g = 16 * rt + gl;    // row within the tile, query row
+        float L = __shfl(lsum, gl, 16), M = __shfl(st.m, gl, 16);
+        float a[SL];
+#pragma unroll
+        for (int i = 0; i < SL; ++i) a[i] = st.o[i][r];
+#pragma unroll
+        for (int v = 0; v < SW - 1; ++v) {
+            const float L1 = sm.ho[v][rt].l[gl], M1 = sm.ho[v][rt].m[gl];
+            const float Mx = fmaxf(M, M1);
+            const float f0 = rescale(M, Mx), f1 = rescale(M1, Mx);
+            L = fmaf(L1, f1, L * f0);
+#pragma unroll
+            for (int i = 0; i < SL; ++i) {
+                const float4 o1 = sm.ho[v][rt].o[i][lane];
+                const float xr = r == 0 ? o1.x : r == 1 ? o1.y : r == 2 ? o1.z : o1.w;
+                a[i] = fmaf(xr, f1, a[i] * f0);
+            }
+            M = Mx;
+        }
+        if (g >= p.R) continue;
+        const size_t slot = row_slot(p, b, kvh, g, x);
+        float inv = L > 0.f ? 1.f / L : 0.f;
+        if constexpr (f8_of(T)) inv *= vmul;
+#pragma unroll
+        for (int i = 0; i < SL; ++i) store_dev(&p.part_o[slot * D + 16 * i + mrow], a[i] * inv);
+        if (mrow == 0) {
+            store_dev(&p.part_m[slot], (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY);
+            store_dev(&p.part_l[slot], L);
+        }
+    }
+}
+
+// Register budget: two waves per SIMD (the merge's loads in flight next to
+// the scan state need more than 128 registers; a grid of one workgroup of
+// four waves per CU, the 32k GQA shape's, holds only one wave per SIMD).
+template <int T, int D, int GMAX, int SW, bool PAGED, bool UNI>
+__global__ void __launch_bounds__(64 * SW) __attribute__((amdgpu_waves_per_eu(2)))
+fused_mfma_kernel(const PartialParams p) {
+    using C = MCfg<D, GMAX, 1>;
+    constexpr int NT = row_tiles(GMAX);
+    static_assert(sizeof(FSmem<D, GMAX, SW>) <= 65536, "LDS budget of one workgroup");
+    __shared__ FSmem<D, GMAX, SW> sm;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's split in the group
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int x = split_index(blockIdx.x, b, kvh, p.Hkv, gridDim.x);        // the group's index in the head
+    const int s = x * SW + w;                                                // this wave's split
+    const int R = p.R, lane = threadIdx.x & 63;
+    const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
+    const int nb = (len + SW * p.split - 1) / (SW * p.split);               // groups holding tokens
+
+    if (x >= nb) {   // none of the group's splits holds a token
+        if (p.flags && lane < R && s < p.max_splits) p.flags[row_slot(p, b, kvh, lane, s)] = 0;
+        if (nb == 0 && x == 0) write_empty_rows<D>(p, b, kvh, 64 * SW);
+        return;
+    }
+
+    const int t0 = s * p.split, t1 = min(t0 + p.split, len);   // t0 >= t1: a split past the request's end
+    float sc, vmul;
+    head_scales<T>(p, kvh, sc, vmul);
+    uint4 qop[NT][C::KS];
+    int lim[NT];
+    load_q_operand<D, GMAX>(p, b, kvh, len, t1, qop, lim);
+    const uint32_t all = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
+    MState<D, GMAX> st[NT];
+    uint32_t badmask = 0;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
+    if (t0 < t1) {
+        if constexpr (UNI) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) st[rt].init(p.phi2);
+            scan_split<T, D, GMAX, 1, PAGED, true>(p, b, kvh, t0, t1, sc, lim, qop, st, sm.tiles[w]);
+            badmask = flagged_rows<GMAX>(st) & all;
+            if (badmask) {   // synchronized recompute of the split
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
+                scan_split<T, D, GMAX, 1, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm.tiles[w]);
+                if (lane == 0 && p.fallback_count) atomicAdd(p.fallback_count, __builtin_popcount(badmask));
+            }
+        } else {
+            scan_split<T, D, GMAX, 1, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm.tiles[w]);
+        }
+    }
+    if (p.flags && lane < R && s < p.max_splits) p.flags[row_slot(p, b, kvh, lane, s)] = (badmask >> lane) & 1u;
+
+    float lsum[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        lsum[rt] = st[rt].l + __shfl_xor(st[rt].l, 16);
+        lsum[rt] += __shfl_xor(lsum[rt], 32);
+    }
+    if constexpr (SW > 1) {
+        __syncthreads();                                  // the hand-over area overlays the tiles
+        if (w > 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i)
+                    sm.ho[w - 1][rt].o[i][lane] = make_float4(st[rt].o[i][0], st[rt].o[i][1], st[rt].o[i][2],
+                                                              st[rt].o[i][3]);
+                if (lane < 16) {
+                    sm.ho[w - 1][rt].l[lane] = lsum[rt];
+                    sm.ho[w - 1][rt].m[lane] = st[rt].m;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (w == 0) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) store_group_partial<T, D, GMAX, SW>(p, st[rt], lsum[rt], sm, rt, b, kvh, x, vmul);
+    }
+    if (arrive_last(&p.tickets[(size_t)b * p.Hkv + kvh], nb, &sm.ticket))
+        merge_rows<D, 64 * SW>(p, b, kvh, nb, sm.merge);
+}
+
+template <int T, int D, int GMAX, int SW, bool PAGED>
+hipError_t launch_fused_shaped(const PartialParams &p, hipStream_t stream) {
+    dim3 grid((p.max_splits + SW - 1) / SW, p.Hkv, p.B);
+    if (p.unified)
+        hipLaunchKernelGGL((fused_mfma_kernel<T, D, GMAX, SW, PAGED, true>), grid, dim3(64 * SW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fused_mfma_kernel<T, D, GMAX, SW, PAGED, false>), grid, dim3(64 * SW), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Splits per workgroup of the single-launch kernel (the host picks 2 or 4).
+template <int T, int D, int GMAX, bool PAGED>
+hipError_t launch_fused(const PartialParams &p, hipStream_t stream) {
+    return p.splits_per_wg == 2 ? launch_fused_shaped<T, D, GMAX, 2, PAGED>(p, stream)
+                                : launch_fused_shaped<T, D, GMAX, 4, PAGED>(p, stream);
 }
 
 // Waves per workgroup, chosen from measurements on MI355X.  A grid of fewer
@@ -715,6 +948,7 @@ hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
 
 template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
+    if (p.tickets) return launch_fused<T, D, GMAX, PAGED>(p, stream);
     if constexpr (GMAX > 4 || !f8_of(T)) {
         if (launch_waves<T>(p) == 1) return launch_shaped<T, D, GMAX, 1, PAGED>(p, stream);
     }

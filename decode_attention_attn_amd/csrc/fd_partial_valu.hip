@@ -27,6 +27,7 @@
 //     the split with SYNC and replaces the partials of exactly the flagged
 //     heads ("The Overflow Fallback: Recomputation").
 #include "fd_device.h"
+#include "fd_merge.h"
 
 namespace fd {
 namespace {
@@ -76,9 +77,10 @@ __device__ __forceinline__ size_t row_offset(const PartialParams &p, int b, int 
     return row * D;
 }
 
-// lim[g]: query row g sees tokens < lim[g] of the split (causal rows)
+// lim[g]: query row g sees tokens < lim[g] of the split (causal rows);
+// sc: the score scale in log2 units (times the KV head's K scale for 8-bit caches)
 template <int DT, int D, int GMAX, bool PAGED, bool UNIFIED>
-__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, const int (&lim)[GMAX],
+__device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t1, float sc, const int (&lim)[GMAX],
                            const float (&qv)[GMAX][Cfg<DT, D, GMAX>::E], State<DT, D, GMAX> &st) {
     using C = Cfg<DT, D, GMAX>;
     constexpr int E = C::E, LPR = C::LPR, RPW = C::RPW, R = C::R;
@@ -111,7 +113,7 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 #pragma unroll
                 for (int e = 0; e < E; ++e) dot = fmaf(qv[g][e], kf[e], dot);
                 dot = group_sum<LPR>(dot);
-                s[r][g] = (ok[r] && tok[r] < lim[g]) ? dot * p.scale_log2 : -INFINITY;
+                s[r][g] = (ok[r] && tok[r] < lim[g]) ? dot * sc : -INFINITY;
             }
         }
         float vf[R][E];
@@ -179,10 +181,11 @@ struct Smem {
     uint32_t bad[kWaves];
 };
 
-// Wave states -> LDS -> the split's partial for the heads in `write_mask`.
-template <int DT, int D, int GMAX>
+// Wave states -> LDS -> the split's partial for the heads in `write_mask`
+// (device-scope stores for the single-launch merge).
+template <int DT, int D, int GMAX, bool FUSED>
 __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Smem<D, GMAX> &sm, int b, int kvh,
-                             int s, uint32_t write_mask) {
+                             int s, uint32_t write_mask, float vmul) {
     using C = Cfg<DT, D, GMAX>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     merge_wave(st);
@@ -213,20 +216,30 @@ __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Sme
         }
         const size_t slot = row_slot(p, b, kvh, g, s);
         float o = L > 0.f ? A / L : 0.f;
-        if constexpr (DT == FP8) o *= p.v_mult;
-        p.part_o[slot * D + dim] = o;
+        if constexpr (DT == FP8) o *= vmul;
+        store_partial<FUSED>(&p.part_o[slot * D + dim], o);
         if (dim == 0) {
-            p.part_m[slot] = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
-            p.part_l[slot] = L;
+            store_partial<FUSED>(&p.part_m[slot], (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY);
+            store_partial<FUSED>(&p.part_l[slot], L);
         }
     }
 }
 
-template <int DT, int D, int GMAX, bool PAGED>
+template <int D, int GMAX>
+union VSmem {
+    Smem<D, GMAX> st;
+    float merge[merge_lds_floats(kFusedMaxRowParts, kMaxGroup, kThreads)];   // the single-launch merge
+};
+
+// FUSED: the single-launch merge (one split per workgroup; the last workgroup
+// of a (request, KV head) merges its splits into out and lse, fd_merge.h).
+template <int DT, int D, int GMAX, bool PAGED, bool FUSED>
 __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
     using C = Cfg<DT, D, GMAX>;
     constexpr int E = C::E;
-    __shared__ Smem<D, GMAX> sm;
+    __shared__ VSmem<D, GMAX> vsm;
+    __shared__ int ticket;
+    Smem<D, GMAX> &sm = vsm.st;
 
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
@@ -236,13 +249,27 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const int t1 = min(t0 + p.split, len);
 
     if (t0 >= t1) {   // empty split: nothing to read
-        if (threadIdx.x < G) {
+        if (threadIdx.x < G && !p.recompute_rows) {
             const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
-            p.part_m[slot] = -INFINITY;
-            p.part_l[slot] = 0.f;
+            if (!FUSED) {
+                p.part_m[slot] = -INFINITY;
+                p.part_l[slot] = 0.f;
+            }
             if (p.flags) p.flags[slot] = 0;
         }
+        if (FUSED && len <= 0 && s == 0) write_empty_rows<D>(p, b, kvh, kThreads);
         return;
+    }
+    // whole-row fallback, second pass: only rows flagged in some split of the request
+    uint32_t rows_to_write = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
+    if (p.recompute_rows) {
+        rows_to_write = rows_flagged_in_request(p, b, kvh, (len + p.split - 1) / p.split);
+        if (!rows_to_write) return;
+    }
+    float sc = p.scale_log2, vmul = p.v_mult;
+    if constexpr (DT == FP8) {
+        if (p.k_scales) sc *= p.k_scales[kvh];
+        if (p.v_scales) vmul = p.v_scales[kvh];
     }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -274,9 +301,9 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const uint32_t all = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
     State<DT, D, GMAX> st;
     uint32_t badmask = 0;
-    if (p.unified) {
+    if (p.unified && !p.recompute_rows) {
         st.init(p.phi2);
-        scan_split<DT, D, GMAX, PAGED, true>(p, b, kvh, t0, t1, lim, qv, st);
+        scan_split<DT, D, GMAX, PAGED, true>(p, b, kvh, t0, t1, sc, lim, qv, st);
         uint32_t mine = 0;
 #pragma unroll
         for (int g = 0; g < GMAX; ++g)
@@ -286,27 +313,38 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) badmask |= sm.bad[w];
         badmask &= all;
-        finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, all & ~badmask);
-        if (badmask) {   // synchronized recompute of the flagged heads
+        // whole-row fallback: every row's unified partial now, the flagged rows'
+        // splits all rewritten by a second pass
+        finish_split<DT, D, GMAX, FUSED>(p, st, sm, b, kvh, s, p.row_fallback ? all : all & ~badmask, vmul);
+        if (badmask && !p.row_fallback) {   // synchronized recompute of the flagged heads
             __syncthreads();
             st.init(-INFINITY);
-            scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, lim, qv, st);
-            finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, badmask);
+            scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qv, st);
+            finish_split<DT, D, GMAX, FUSED>(p, st, sm, b, kvh, s, badmask, vmul);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
     } else {
         st.init(-INFINITY);
-        scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, lim, qv, st);
-        finish_split<DT, D, GMAX>(p, st, sm, b, kvh, s, all);
+        scan_split<DT, D, GMAX, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qv, st);
+        finish_split<DT, D, GMAX, FUSED>(p, st, sm, b, kvh, s, rows_to_write, vmul);
     }
-    if (p.flags && threadIdx.x < G) p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
+    if (p.flags && threadIdx.x < G && !p.recompute_rows)
+        p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
+    if constexpr (FUSED) {
+        const int nb = (len + p.split - 1) / p.split;       // splits holding tokens
+        __syncthreads();                                     // the merge area overlays the epilogue's
+        if (arrive_last(&p.tickets[(size_t)b * p.Hkv + kvh], nb, &ticket)) merge_rows<D, kThreads>(p, b, kvh, nb, vsm.merge);
+    }
 }
 
 template <int DT, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
     dim3 grid(p.max_splits, p.Hkv, p.B);
-    hipLaunchKernelGGL((partial_valu_kernel<DT, D, GMAX, PAGED>), grid, dim3(kThreads), 0, stream, p);
+    if (p.tickets)
+        hipLaunchKernelGGL((partial_valu_kernel<DT, D, GMAX, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((partial_valu_kernel<DT, D, GMAX, PAGED, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -40,7 +40,8 @@
  *    FD_ERR_UNSUPPORTED).
  *  - 8-bit caches (FD_FP8_E4M3, OCP FP8 E4M3: bias 7, no infinities, largest
  *    finite 448, S.1111.111 = NaN) stand for stored * k_scale and
- *    stored * v_scale (one scale per tensor); the handbook page lists caches
+ *    stored * v_scale, with one scale per tensor or one per KV head
+ *    (desc->k_scales, desc->v_scales); the handbook page lists caches
  *    stored in FP8, read in wide loads and converted in registers (section
  *    "A paged decode attention kernel (with GQA)", its list of improvements).
  *  - GQA: query head h reads KV head h / (Hq / Hkv); consecutive query heads
@@ -96,6 +97,16 @@ typedef enum fd_dtype { FD_F32 = 0, FD_F16 = 1, FD_BF16 = 2, FD_FP8_E4M3 = 3 /* 
  *   Unified Max Value", Eq. 3 and 4, "The Overflow Fallback: Recomputation"). */
 typedef enum fd_softmax_mode { FD_SOFTMAX_SYNC = 0, FD_SOFTMAX_UNIFIED_MAX = 1 } fd_softmax_mode;
 
+/* What UNIFIED_MAX recomputes with SYNC when a score leaves [lo, hi].
+ * SPLIT: the flagged split only, inside the partial kernel (exact, since the
+ *   merge of split partials is exact).
+ * ROW: every split of a query row that has a flagged split -- the
+ *   FlashDecoding++ page's own granularity ("The Overflow Fallback:
+ *   Recomputation" recomputes the whole attention row) -- by a second,
+ *   synchronized launch over the flagged rows; needs flags (not NULL) and
+ *   the separate merge. */
+typedef enum fd_fallback { FD_FALLBACK_SPLIT = 0, FD_FALLBACK_ROW = 1 } fd_fallback;
+
 /* Which split-partial kernel runs.  Every choice computes the same result to
  * within floating-point rounding. */
 typedef enum fd_kernel {
@@ -104,6 +115,23 @@ typedef enum fd_kernel {
     FD_KERNEL_MFMA = 2   /* matrix cores; 16- and 8-bit caches, d in {64, 128}, pages of a
                             multiple of 16 tokens; not with f16 q in UNIFIED_MAX mode */
 } fd_kernel;
+
+/* How the split partials are merged by fd_decode_attn and fd_decode_attn_paged.
+ * SEPARATE: a second kernel launch merges them (the Flash-Decoding page's
+ *   "Hardware Execution Topology and Memory Traffic": partials to global
+ *   memory, then a reduction kernel).
+ * FUSED: one launch; the last workgroup of each (request, KV head) to finish
+ *   merges that head's partials (the FlashDecoding++ page, "Asynchronized
+ *   Softmax with Unified Max Value", its design choices: a reduction across
+ *   workers by atomics instead of a relaunch).  Needs the workspace's ticket
+ *   area to be zero when the call starts (see fd_workspace_bytes); requires
+ *   B * Hkv <= 65536 and reports shapes whose merge does not fit one
+ *   workgroup, and FD_FALLBACK_ROW, FD_ERR_UNSUPPORTED.
+ * AUTO: whichever the library measured faster for the shape.
+ * Both give the same result to within floating-point rounding (the merge is
+ * exact; FUSED takes it as a tree: the splits of a workgroup, then the
+ * workgroups).  fd_decode_attn_partial and fd_decode_attn_combine ignore it. */
+typedef enum fd_merge { FD_MERGE_AUTO = 0, FD_MERGE_SEPARATE = 1, FD_MERGE_FUSED = 2 } fd_merge;
 
 typedef struct fd_decode_desc {
     int32_t B, Hq, Hkv, d;   /* batch, query heads, KV heads, head dimension */
@@ -124,12 +152,19 @@ typedef struct fd_decode_desc {
     float k_scale, v_scale;  /* FD_FP8_E4M3 caches: a stored K / V value stands for
                                 stored * scale; <= 0 selects 1; ignored otherwise */
     int32_t q_len;           /* query tokens per request, causal; <= 0 selects 1 */
+    const float *k_scales;   /* FD_FP8_E4M3 caches: NULL, or a device array [Hkv] of per-KV-head K
+                                scales replacing k_scale (values finite and > 0, not checked);
+                                4-byte aligned; ignored for other caches */
+    const float *v_scales;   /* the same for V, replacing v_scale */
+    int32_t merge;           /* fd_merge */
+    int32_t fallback;        /* fd_fallback (UNIFIED_MAX only) */
 } fd_decode_desc;
 
 /* Split-partial kernel over a contiguous cache.
  *   k, v          : [B, kv_capacity, Hkv, d] of kv_dtype
  *   part_o/m/l    : as in the conventions above (written for every split < max_splits)
- *   flags         : uint8 [B, q_len, Hq, max_splits] or NULL; UNIFIED_MAX writes 1 for a
+ *   flags         : uint8 [B, q_len, Hq, max_splits] or NULL (required by
+ *                   FD_FALLBACK_ROW); UNIFIED_MAX writes 1 for a
  *                   (request, query head, split) whose scores left [lo, hi], else 0
  *   fallback_count: int32 [1] or NULL; UNIFIED_MAX adds the number of flagged
  *                   (request, query head, split) triples (set it to 0 first for
@@ -152,7 +187,19 @@ fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float *part_o
                                  const float *part_l, const int32_t *seq_lens, void *out, float *lse,
                                  void *stream);
 
-/* Partial + combine over a paged cache (page "FlashAttention and inference
+/* Partial + merge over a contiguous cache: fd_decode_attn_partial followed by
+ * fd_decode_attn_combine, or the single launch (desc->merge), with the
+ * partials in the caller's workspace (layout as for fd_decode_attn_paged).
+ *   k, v : [B, kv_capacity, Hkv, d] of kv_dtype
+ *   out, lse, flags, fallback_count : as for the entry points above.
+ * Split partials are the Flash-Decoding page's "Mathematical Formulation of
+ * Split-KV Parallelism", their merge its "The Rescaling and Online Softmax
+ * Reduction Algorithm". */
+fd_status fd_decode_attn(const fd_decode_desc *desc, const void *q, const void *k, const void *v,
+                         int32_t kv_capacity, const int32_t *seq_lens, void *workspace, size_t workspace_bytes,
+                         void *out, float *lse, uint8_t *flags, int32_t *fallback_count, void *stream);
+
+/* Partial + merge over a paged cache (page "FlashAttention and inference
  * kernels", section "PagedAttention": token t of request b lives at slot
  * t % page_size of physical block block_table[b][t / page_size]).
  *   k_cache, v_cache : [num_pages, page_size, Hkv, d] of kv_dtype
@@ -161,8 +208,12 @@ fd_status fd_decode_attn_combine(const fd_decode_desc *desc, const float *part_o
  *                      [0, num_pages) is never dereferenced: its tokens count
  *                      as absent.
  *   workspace        : >= fd_workspace_bytes(desc) bytes of device memory, 256-byte
- *                      aligned; holds part_o, part_m, part_l in that order, each
- *                      starting on a 256-byte boundary.
+ *                      aligned: FD_TICKET_BYTES of merge counters, then part_o,
+ *                      part_m and part_l, each starting on a 256-byte boundary.
+ *                      The counters must be zero before the first single-launch
+ *                      call on a workspace (allocate it zeroed, or clear the
+ *                      first FD_TICKET_BYTES once); every completed call leaves
+ *                      them zero.  Calls that overlap on one workspace race.
  *   flags, fallback_count : as for fd_decode_attn_partial.
  * split_size must be a multiple of page_size so that split boundaries fall on
  * page boundaries (Flash-Decoding page, "Production Implementation Guidelines"). */
@@ -194,7 +245,11 @@ fd_status fd_decode_attn_paged_noalloc(const fd_decode_desc *desc, const void *q
                                        const int32_t *seq_lens, void *out, float *lse, uint8_t *flags,
                                        int32_t *fallback_count, void *stream);
 
-/* Bytes of workspace fd_decode_attn_paged needs for `desc` (0 for an invalid desc). */
+/* Bytes of the merge counters at the start of a workspace. */
+#define FD_TICKET_BYTES (65536u * 4u)
+
+/* Bytes of workspace fd_decode_attn and fd_decode_attn_paged need for `desc`
+ * (0 for an invalid desc): the counters plus the fp32 partials. */
 size_t fd_workspace_bytes(const fd_decode_desc *desc);
 
 /* Host-only split choice, no GPU call.  Work units W = B * Hkv (one workgroup

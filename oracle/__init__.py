@@ -33,7 +33,8 @@ class OracleProblem(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("dtype", C.c_int32), ("N", C.c_int32), ("page_size", C.c_int32),
                 ("max_blocks", C.c_int32), ("scale", C.c_double), ("q_dtype", C.c_int32),
-                ("k_scale", C.c_double), ("v_scale", C.c_double), ("q_len", C.c_int32)]
+                ("k_scale", C.c_double), ("v_scale", C.c_double), ("q_len", C.c_int32),
+                ("k_scales", C.c_void_p), ("v_scales", C.c_void_p)]
 
 
 def build() -> Path:
@@ -62,7 +63,7 @@ def lib():
         L.oracle_out_of_range.argtypes = [C.c_double, C.c_double, C.c_double]
         L.oracle_unified_max.argtypes = [pp, vp, vp, vp, i32p, i32p, C.c_int, C.c_int, C.c_double, C.c_double,
                                          C.c_double, i32p, C.c_int, C.c_int, dp, dp, dp,
-                                         C.POINTER(C.c_uint8), dp, dp, C.POINTER(C.c_longlong)]
+                                         C.POINTER(C.c_uint8), dp, dp, C.POINTER(C.c_longlong), C.c_int]
         L.oracle_decode.argtypes = [C.c_int, vp, C.c_size_t, dp]
         for f in ("oracle_attention", "oracle_split_partials", "oracle_merge", "oracle_merge_lse",
                   "oracle_online_tiles", "oracle_out_of_range", "oracle_unified_max"):
@@ -122,15 +123,26 @@ def _i32(a):
 
 
 def problem(B, Hq, Hkv, d, dtype, N=0, page_size=0, max_blocks=0, scale=None, q_dtype=None, k_scale=1.0,
-            v_scale=1.0, q_len=1):
+            v_scale=1.0, q_len=1, k_scales=None, v_scales=None):
     """dtype: storage of K and V; q_dtype: storage of q (default: dtype; bf16 for fp8 caches);
-    q_len query tokens per request (q [B, q_len, Hq, d]; results by row (b*q_len + i)*Hq + h)."""
+    q_len query tokens per request (q [B, q_len, Hq, d]; results by row (b*q_len + i)*Hq + h).
+    k_scales / v_scales: per-KV-head scales [Hkv] replacing k_scale / v_scale."""
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     if q_dtype is None:
         q_dtype = "bf16" if dtype == "fp8" else dtype
-    return OracleProblem(B, Hq, Hkv, d, DTYPE_CODE[dtype], N, page_size, max_blocks, float(scale),
-                         DTYPE_CODE[q_dtype], float(k_scale), float(v_scale), int(q_len))
+    p = OracleProblem(B, Hq, Hkv, d, DTYPE_CODE[dtype], N, page_size, max_blocks, float(scale),
+                      DTYPE_CODE[q_dtype], float(k_scale), float(v_scale), int(q_len), None, None)
+    keep = []
+    for name, arr in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if arr is not None:
+            a = np.ascontiguousarray(arr, dtype=np.float64)
+            if a.shape != (Hkv,):
+                raise ValueError(f"{name} must have shape ({Hkv},)")
+            keep.append(a)
+            setattr(p, name, a.ctypes.data)
+    p._keep = keep          # the arrays live as long as the problem
+    return p
 
 
 def problem_of(inp, scale=None):
@@ -138,7 +150,8 @@ def problem_of(inp, scale=None):
     w = inp.w
     return problem(w.B, w.Hq, w.Hkv, w.d, w.dtype, N=w.N, page_size=w.page_size,
                    max_blocks=w.max_blocks if w.page_size else 0, scale=scale, q_dtype=w.q_dtype,
-                   k_scale=w.k_scale, v_scale=w.v_scale, q_len=w.q_len)
+                   k_scale=w.k_scale, v_scale=w.v_scale, q_len=w.q_len,
+                   k_scales=getattr(w, "k_scales", None), v_scales=getattr(w, "v_scales", None))
 
 
 def _nrows(p):
@@ -221,9 +234,11 @@ def out_of_range(s, lo, hi) -> bool:
 
 
 def unified_max(p, q, k, v, split, S_max, phi, lo, hi, seq_lens=None, block_table=None, rows=None,
-                threads=None):
-    """Unified-max softmax with per-split fallback.  Returns a dict with out, lse,
-    part_o/part_m/part_l, flags [B*Hq, S_max] (uint8) and n_flagged."""
+                threads=None, whole_row=False):
+    """Unified-max softmax with fallback: per split, or with whole_row every
+    split of a row that has a flagged split.  Returns a dict with out, lse,
+    part_o/part_m/part_l, flags [B*Hq, S_max] (uint8: the splits whose scores
+    left the range) and n_flagged."""
     dtype = _NAME[p.dtype]
     q, k, v = _storage(q, _NAME[p.q_dtype]), _storage(k, dtype), _storage(v, dtype)
     sl, bt = _i32(seq_lens), _i32(block_table)
@@ -240,7 +255,7 @@ def unified_max(p, q, k, v, split, S_max, phi, lo, hi, seq_lens=None, block_tabl
                                   split, S_max, float(phi), float(lo), float(hi), _ptr(r, C.c_int32), nr,
                                   threads or default_threads(), _ptr(po, C.c_double), _ptr(pm, C.c_double),
                                   _ptr(pl, C.c_double), _ptr(fl, C.c_uint8), _ptr(out, C.c_double),
-                                  _ptr(lse, C.c_double), C.byref(nf))
+                                  _ptr(lse, C.c_double), C.byref(nf), int(bool(whole_row)))
     _check(rc, "oracle_unified_max")
     return dict(out=out, lse=lse, part_o=po, part_m=pm, part_l=pl, flags=fl, n_flagged=nf.value)
 

@@ -37,7 +37,9 @@
  *   kernel (with GQA)", its list of improvements; section on the KV cache's
  *   size names KV cache quantization).  The format is OCP FP8 E4M3 (OCP 8-bit
  *   Floating Point Specification, "E4M3"); a stored K or V value means
- *   stored * k_scale or stored * v_scale (one scale per tensor).
+ *   stored * k_scale or stored * v_scale, with one scale per tensor or, when
+ *   per-head arrays are given, one per KV head (the scale of KV head kvh
+ *   multiplies every element of that head's rows).
  *   several query tokens per request (verification of drafted tokens, or a
  *   chunk of new tokens whose K and V are already in the cache): the causal
  *   mask of the handbook's FlashAttention forward kernel (section
@@ -53,7 +55,9 @@
  *     a bound is in range (the FlashDecoding++ worked example passes 9-6 = 3
  *     = b); a split is flagged iff some score s < lo or s > hi;
  *   - the fallback recomputes the flagged split only (its merge is exact, so
- *     the result does not depend on this choice).
+ *     the result does not depend on this choice); whole_row = 1 takes the
+ *     page's own granularity instead: a row with any flagged split has every
+ *     one of its splits recomputed with the synchronized softmax.
  *
  * Parity pins for every function live in tests/test_oracle.py.
  */
@@ -84,7 +88,13 @@ typedef struct {
     double k_scale;      /* a stored K value means stored * k_scale            */
     double v_scale;      /* a stored V value means stored * v_scale            */
     int32_t q_len;       /* query tokens per request (q is [B][q_len][Hq][d]) */
+    const double *k_scales;  /* [Hkv] or NULL: per-KV-head K scales, replacing k_scale */
+    const double *v_scales;  /* [Hkv] or NULL: per-KV-head V scales, replacing v_scale */
 } oracle_problem;
+
+/* the scale a stored K / V value of KV head kvh is multiplied by */
+static double k_scale_of(const oracle_problem *p, int kvh) { return p->k_scales ? p->k_scales[kvh] : p->k_scale; }
+static double v_scale_of(const oracle_problem *p, int kvh) { return p->v_scales ? p->v_scales[kvh] : p->v_scale; }
 
 /* ---------------------------------------------------------------------- */
 /* exact decoding of the storage types                                     */
@@ -167,6 +177,10 @@ static int check_problem(const oracle_problem *p, const int32_t *seq_lens, const
     if (p->q_dtype < ODT_F32 || p->q_dtype > ODT_BF16) return ORACLE_EINVAL;
     if (!(p->k_scale > 0.0) || !(p->v_scale > 0.0) || isinf(p->k_scale) || isinf(p->v_scale))
         return ORACLE_EINVAL;
+    for (int h = 0; h < p->Hkv; ++h)
+        if (!(k_scale_of(p, h) > 0.0) || !(v_scale_of(p, h) > 0.0) || isinf(k_scale_of(p, h)) ||
+            isinf(v_scale_of(p, h)))
+            return ORACLE_EINVAL;
     if (p->page_size < 0) return ORACLE_EINVAL;
     if (p->page_size > 0 && (!block_table || p->max_blocks <= 0)) return ORACLE_EINVAL;
     for (int b = 0; b < p->B; ++b) {
@@ -201,12 +215,13 @@ static void scores(const oracle_problem *p, const void *q, const void *k, const 
                    int r, int b, int h, int t0, int t1, double *s)
 {
     int kvh = h / (p->Hq / p->Hkv);
+    double ks = k_scale_of(p, kvh);
     size_t qoff = (size_t)r * (size_t)p->d;
     for (int t = t0; t < t1; ++t) {
         size_t koff = kv_row(p, block_table, b, t, kvh);
         double dot = 0.0;
         for (int i = 0; i < p->d; ++i)
-            dot += elem(q, p->q_dtype, qoff + i) * (p->k_scale * elem(k, p->dtype, koff + i));
+            dot += elem(q, p->q_dtype, qoff + i) * (ks * elem(k, p->dtype, koff + i));
         s[t - t0] = dot * p->scale;
     }
 }
@@ -219,6 +234,7 @@ static double weighted_v(const oracle_problem *p, const void *v, const int32_t *
                          int b, int h, int t0, int t1, double *s, double c, double *o)
 {
     int kvh = h / (p->Hq / p->Hkv);
+    double vs = v_scale_of(p, kvh);
     double den = 0.0;
     for (int t = t0; t < t1; ++t) {
         s[t - t0] = exp(s[t - t0] - c);
@@ -227,7 +243,7 @@ static double weighted_v(const oracle_problem *p, const void *v, const int32_t *
     for (int i = 0; i < p->d; ++i) o[i] = 0.0;
     for (int t = t0; t < t1; ++t) {
         size_t voff = kv_row(p, block_table, b, t, kvh);
-        for (int i = 0; i < p->d; ++i) o[i] += s[t - t0] * (p->v_scale * elem(v, p->dtype, voff + i));
+        for (int i = 0; i < p->d; ++i) o[i] += s[t - t0] * (vs * elem(v, p->dtype, voff + i));
     }
     for (int i = 0; i < p->d; ++i) o[i] = den > 0.0 ? o[i] / den : 0.0;
     return den;
@@ -467,7 +483,7 @@ int oracle_unified_max(const oracle_problem *p, const void *q, const void *k, co
                        double phi, double lo, double hi,
                        const int32_t *rows, int n_rows, int n_threads,
                        double *part_o, double *part_m, double *part_l, uint8_t *flags,
-                       double *out, double *lse, long long *n_flagged)
+                       double *out, double *lse, long long *n_flagged, int whole_row)
 {
     int rc = check_problem(p, seq_lens, block_table);
     if (rc) return rc;
@@ -491,6 +507,16 @@ int oracle_unified_max(const oracle_problem *p, const void *q, const void *k, co
             failed = 1;
             continue;
         }
+        /* whole_row: first the range check of every split of the row */
+        int row_bad = 0;
+        if (whole_row) {
+            for (int sp = 0; sp < S_max; ++sp) {
+                int t0 = sp * split, t1 = t0 + split < n ? t0 + split : n;
+                if (t0 >= t1) continue;
+                scores(p, q, k, block_table, r, b, h, t0, t1, s);
+                for (int t = 0; t < t1 - t0; ++t) row_bad |= oracle_out_of_range(s[t], lo, hi);
+            }
+        }
         for (int sp = 0; sp < S_max; ++sp) {
             size_t slot = (size_t)r * S_max + sp;
             double *o = part_o + slot * p->d;
@@ -505,10 +531,12 @@ int oracle_unified_max(const oracle_problem *p, const void *q, const void *k, co
             scores(p, q, k, block_table, r, b, h, t0, t1, s);
             int bad = 0;
             for (int t = 0; t < t1 - t0; ++t) bad |= oracle_out_of_range(s[t], lo, hi);
-            double c = phi;
-            if (bad) {                        /* synchronized recompute */
+            if (bad) {
                 flags[slot] = 1;
                 ++count;
+            }
+            double c = phi;
+            if (whole_row ? row_bad : bad) {  /* synchronized recompute: the split's own maximum */
                 c = s[0];
                 for (int t = 1; t < t1 - t0; ++t) c = s[t] > c ? s[t] : c;
             }

@@ -107,9 +107,10 @@ _STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.u
 _CHUNK = 1 << 20
 
 
-def normal(seed: int, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
+def normal(seed: int, shape, dtype: str, scale=1.0) -> np.ndarray:
     """Standard normal draws from PCG64(seed), rounded to `dtype` storage
-    (fp8: the draw divided by `scale`, see the module docstring).
+    (fp8: the draw divided by `scale`, see the module docstring; `scale` may
+    also be one value per KV head, shape[-2] of them, for per-head scales).
 
     Drawn in chunks through reused buffers (one pass over the output, no
     full-size temporaries); the values are the generator's sequence in order.
@@ -134,7 +135,11 @@ def normal(seed: int, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
             np.right_shift(tm, 16, out=tm)
             flat[i:i + m] = tm
         elif dtype == "fp8":
-            flat[i:i + m] = f32_to_e4m3_bits(buf[:m] / np.float32(scale))
+            if np.ndim(scale) == 0:
+                flat[i:i + m] = f32_to_e4m3_bits(buf[:m] / np.float32(scale))
+            else:   # element j belongs to KV head (j // d) % Hkv
+                heads = (np.arange(i, i + m, dtype=np.int64) // shape[-1]) % shape[-2]
+                flat[i:i + m] = f32_to_e4m3_bits(buf[:m] / np.asarray(scale, np.float32)[heads])
         else:
             flat[i:i + m] = buf[:m]
     return out
@@ -163,6 +168,8 @@ class Workload:
     k_scale: float = 1.0                # fp8 caches: a stored K value stands for stored * k_scale
     v_scale: float = 1.0
     q_len: int = 1                      # query tokens per request: q [B, q_len, Hq, d]
+    k_scales: Optional[tuple] = None    # fp8 caches: one K scale per KV head, replacing k_scale
+    v_scales: Optional[tuple] = None    # fp8 caches: one V scale per KV head, replacing v_scale
 
     @property
     def q_dtype(self) -> str:
@@ -195,6 +202,11 @@ WORKLOADS = {
     # the long-context GQA shape with an 8-bit cache (scale 1/64: N(0, 1) draws stored as 64 x)
     "long_gqa_32k_fp8": Workload("long_gqa_32k_fp8", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256,
                                  N=32768, k_scale=1.0 / 64, v_scale=1.0 / 64),
+    # the same with one scale per KV head (distinct, not powers of two)
+    "long_gqa_32k_fp8_head_scales": Workload(
+        "long_gqa_32k_fp8_head_scales", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256, N=32768,
+        k_scales=tuple(c / 64 for c in (0.75, 1.25, 0.9, 1.1, 0.8, 1.2, 0.95, 1.05)),
+        v_scales=tuple(c / 64 for c in (1.3, 0.7, 1.15, 0.85, 1.05, 0.95, 0.6, 1.4))),
     # the long-context GQA shape verifying 4 drafted tokens (4 x 4 query rows per KV head)
     "long_gqa_32k_verify4": Workload("long_gqa_32k_verify4", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256,
                                      N=32768, q_len=4),
@@ -266,8 +278,8 @@ def make_inputs(w: Workload, poison_tail: bool = True) -> Inputs:
         shape = (P, w.page_size, w.Hkv, w.d)
     else:
         shape = (w.B, w.N, w.Hkv, w.d)
-    k = normal(SEED_K, shape, w.dtype, w.k_scale)
-    v = normal(SEED_V, shape, w.dtype, w.v_scale)
+    k = normal(SEED_K, shape, w.dtype, w.k_scales if w.k_scales is not None else w.k_scale)
+    v = normal(SEED_V, shape, w.dtype, w.v_scales if w.v_scales is not None else w.v_scale)
 
     mask = None
     if w.stress_frac > 0:

@@ -88,17 +88,28 @@ class Run:
         self.table = t.from_numpy(inp.block_table).to("cuda") if inp.block_table is not None else None
 
     def desc(self, split=None, mode="sync", phi=0.0, lo=0.0, hi=0.0, kernel="auto", out_dtype=None,
-             max_splits=None):
+             max_splits=None, merge="auto", fallback="split"):
         w = self.w
         split = split or w.split
-        f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale) if w.dtype == "fp8" else {}
+        f8 = {}
+        if w.dtype == "fp8":
+            f8 = dict(q_dtype=w.q_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+            t = torch()
+            if w.k_scales is not None:
+                self._ks = t.tensor(w.k_scales, dtype=t.float32, device="cuda")
+                f8["k_scales"] = self._ks
+            if w.v_scales is not None:
+                self._vs = t.tensor(w.v_scales, dtype=t.float32, device="cuda")
+                f8["v_scales"] = self._vs
         return fd.make_desc(w.B, w.Hq, w.Hkv, w.d, w.dtype, out_dtype, split_size=split,
                             max_splits=max_splits or max(1, -(-w.N // split)), mode=mode, phi=phi, lo=lo,
-                            hi=hi, kernel=kernel, q_len=w.q_len, **f8)
+                            hi=hi, kernel=kernel, q_len=w.q_len, merge=merge, fallback=fallback, **f8)
 
-    def run(self, use_lens=True, **kw):
-        """Partial + combine (contiguous) or the paged entry point.  Returns a dict
-        of float64 numpy results shaped by rows r = b * Hq + h."""
+    def run(self, use_lens=True, full=False, workspace=None, **kw):
+        """Partial + combine (contiguous), the paged entry point, or with
+        full=True the contiguous fd_decode_attn (merge as kw["merge"] says).
+        Returns a dict of float64 numpy results shaped by rows r = b * Hq + h
+        (partials are the workspace's when the merge is the single launch)."""
         t = torch()
         w = self.w
         desc = self.desc(**kw)
@@ -110,16 +121,15 @@ class Run:
         count = t.zeros(1, dtype=t.int32, device="cuda")
         lens = self.lens if use_lens else None
         if w.page_size:
-            ws = fd.alloc_workspace(desc)
+            ws = fd.alloc_workspace(desc) if workspace is None else workspace
             fd.fd_decode_attn_paged(desc, self.q, self.k, self.v, w.page_size, self.table, self.lens, ws, out,
                                     lse, flags, count)
-            n = w.B * QR * S
-            o_bytes = (n * w.d * 4 + 255) // 256 * 256
-            m_bytes = (n * 4 + 255) // 256 * 256
-            fw = ws.view(t.float32)
-            po = fw[:n * w.d].view(w.B, QR, S, w.d)
-            pm = fw[o_bytes // 4:o_bytes // 4 + n].view(w.B, QR, S)
-            pl = fw[(o_bytes + m_bytes) // 4:(o_bytes + m_bytes) // 4 + n].view(w.B, QR, S)
+            po, pm, pl = fd.workspace_partials(desc, ws)
+        elif full:
+            ws = fd.alloc_workspace(desc) if workspace is None else workspace
+            fd.fd_decode_attn(desc, self.q, self.k, self.v, w.N, self.lens if use_lens else None, ws, out, lse,
+                              flags, count)
+            po, pm, pl = fd.workspace_partials(desc, ws)
         else:
             po, pm, pl, _ = fd.alloc_partials(desc)
             fd.fd_decode_attn_partial(desc, self.q, self.k, self.v, w.N, lens, po, pm, pl, flags, count)

@@ -15,7 +15,7 @@ HEADER = Path(__file__).resolve().parents[1] / "include" / "fd_decode_attn.h"
 
 
 def declared_functions():
-    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)   # declarations, not comments
     return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
 
 
@@ -44,7 +44,7 @@ def test_desc_struct_matches_header_field_order():
         if not decl:
             continue
         names = decl.split(None, 1)[1]
-        fields += [n.strip() for n in names.split(",")]
+        fields += [re.sub(r"^.*?\**\s*(\w+)$", r"\1", n.strip().split()[-1]) for n in names.split(",")]
     assert fields == [f[0] for f in fd.fd_decode_desc._fields_]
 
 
@@ -122,7 +122,7 @@ def test_workspace_bytes_layout(golden):
     d = fd.make_desc(1, 32, 8, 128, "bf16", split_size=256, max_splits=128)
     rows = 1 * 32 * 128
     r256 = lambda x: (x + 255) // 256 * 256
-    assert fd.fd_workspace_bytes(d) == r256(rows * 128 * 4) + 2 * r256(rows * 4)
+    assert fd.fd_workspace_bytes(d) == fd.TICKET_BYTES + r256(rows * 128 * 4) + 2 * r256(rows * 4)
     # the page's intermediate-buffer example counts 16-bit O; ours is fp32, twice it
     g = golden("flashdecoding_split_sizes.json")["intermediate_buffer_example"]
     assert g["B"] * g["H"] * g["S"] * g["d"] * g["elem_bytes"] == g["bytes"]
@@ -213,7 +213,8 @@ def test_multi_query_descriptor_validation():
     zero = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=0)
     four = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=4)
     assert fd.fd_workspace_bytes(zero) == fd.fd_workspace_bytes(one)
-    assert fd.fd_workspace_bytes(four) >= 4 * fd.fd_workspace_bytes(one) - 3 * 256 * 3
+    T = fd.TICKET_BYTES
+    assert fd.fd_workspace_bytes(four) - T >= 4 * (fd.fd_workspace_bytes(one) - T) - 3 * 256 * 3
 
 
 def test_empty_batch_is_a_no_op():
@@ -293,3 +294,54 @@ def test_paged_rejects_misaligned_pointers(pos, off):
             _addr(8), C.c_size_t(ws), _addr(10), _addr(11), _addr(12), _addr(13)]
     args[pos] = _addr(pos, off)
     assert L.fd_decode_attn_paged(C.byref(desc), *args, None) == fd.FD_ERR_INVALID_ARG
+
+
+def test_full_entry_point_validation():
+    """fd_decode_attn: bad merge codes, misaligned pointers, a short workspace,
+    and single-launch shapes beyond the counter area, all before any launch."""
+    L = fd.lib()
+    desc = fd.make_desc(2, 8, 8, 128, "bf16", split_size=256, max_splits=4)
+    ws = fd.fd_workspace_bytes(desc)
+    good = [_addr(0), _addr(1), _addr(2), C.c_int32(1024), _addr(4), _addr(5), C.c_size_t(ws), _addr(7), _addr(8),
+            _addr(9), _addr(10)]
+
+    def call(d, args):
+        return L.fd_decode_attn(C.byref(d), *args, None)
+
+    bad = fd.make_desc(2, 8, 8, 128, "bf16", split_size=256, max_splits=4)
+    bad.merge = 3
+    assert call(bad, good) == fd.FD_ERR_INVALID_ARG
+    for pos, off in [(0, 8), (1, 4), (2, 2), (4, 2), (5, 16), (7, 8), (8, 2), (10, 2)]:
+        args = list(good)
+        args[pos] = _addr(pos, off)
+        assert call(desc, args) == fd.FD_ERR_INVALID_ARG, pos
+    args = list(good)
+    args[6] = C.c_size_t(ws - 1)
+    assert call(desc, args) == fd.FD_ERR_WORKSPACE_TOO_SMALL
+    # 65535 requests x 2 KV heads: more (request, KV head) counters than the area holds
+    big = fd.make_desc(65535, 2, 2, 128, "bf16", split_size=256, max_splits=1, merge="fused")
+    args = list(good)
+    args[6] = C.c_size_t(fd.fd_workspace_bytes(big))
+    assert call(big, args) == fd.FD_ERR_UNSUPPORTED
+    assert fd.fd_workspace_bytes(desc) == fd.TICKET_BYTES + 2 * 8 * 4 * 128 * 4 + 2 * 256
+
+
+def test_whole_row_fallback_validation():
+    """FD_FALLBACK_ROW needs flags (its second pass reads them) and the
+    separate merge; an unknown fallback code is refused."""
+    L = fd.lib()
+    desc = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, mode="unified", phi=-6.0, lo=-6.0, hi=6.0,
+                        fallback="row")
+    args = [_addr(i) for i in range(10)]
+    args[3] = C.c_int32(16)
+    args[8] = None                            # flags
+    assert L.fd_decode_attn_partial(C.byref(desc), *args, None) == fd.FD_ERR_INVALID_ARG
+    fused = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, mode="unified", phi=-6.0, lo=-6.0, hi=6.0,
+                         fallback="row", merge="fused")
+    ws = fd.fd_workspace_bytes(fused)
+    full = [_addr(0), _addr(1), _addr(2), C.c_int32(1024), _addr(4), _addr(5), C.c_size_t(ws), _addr(7), _addr(8),
+            _addr(9), _addr(10)]
+    assert L.fd_decode_attn(C.byref(fused), *full, None) == fd.FD_ERR_UNSUPPORTED
+    bad = fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4)
+    bad.fallback = 2
+    assert _partial_status(bad) == fd.FD_ERR_INVALID_ARG

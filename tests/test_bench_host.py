@@ -72,8 +72,21 @@ def test_counter_bytes_are_scaled_by_the_calibration_copy(tmp_path, monkeypatch)
     assert d["fetch_scale"] == pytest.approx(2.0) and d["write_scale"] == pytest.approx(1.0)
     expect = 1001.0 * 1024 * 2.0 + 10.0 * 1024 * 1.0
     assert d["kernels"][bench.PARTIAL_KERNEL]["hbm_bytes_per_launch"] == pytest.approx(expect)
-    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, settings) == pytest.approx(expect)
+    assert bench.traffic_from_profile("wl", [bench.PARTIAL_KERNEL], settings) == pytest.approx(expect)
+    # a call of two kernels sums them; a kernel without counters gives none
+    assert bench.traffic_from_profile("wl", [bench.PARTIAL_KERNEL, bench.PARTIAL_KERNEL], settings) == \
+        pytest.approx(2 * expect)
+    assert bench.traffic_from_profile("wl", [bench.PARTIAL_KERNEL, "combine"], settings) is None
     # other settings, or other kernel sources, make the stored figure stale
-    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, {"kernel": "valu", "mode": "sync"}) is None
+    assert bench.traffic_from_profile("wl", [bench.PARTIAL_KERNEL], {"kernel": "valu", "mode": "sync"}) is None
     monkeypatch.setattr(bench, "source_hash", lambda: "changed")
-    assert bench.traffic_from_profile("wl", bench.PARTIAL_KERNEL, settings) is None
+    assert bench.traffic_from_profile("wl", [bench.PARTIAL_KERNEL], settings) is None
+
+
+def test_kernel_keys():
+    assert bench.kernel_key("void fd::(anonymous namespace)::fused_mfma_kernel<2, 128, 4, 4, false, false>"
+                            "(fd::PartialParams)") == "fused"
+    assert bench.kernel_key("void fd::(anonymous namespace)::partial_valu_kernel<2, 128, 4, false, true>"
+                            "(fd::PartialParams)") == bench.PARTIAL_KERNEL
+    assert bench.kernel_key("void fd::(anonymous namespace)::combine_kernel<128, 128, 256, true>"
+                            "(fd::CombineParams)") == "combine"

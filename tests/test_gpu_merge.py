@@ -118,3 +118,121 @@ def test_combine_batch_with_lengths_reads_only_each_requests_splits():
     ft.assert_close(out, ref, "f32", "combine out")
     ft.assert_close(lse, lref, "f32", "combine lse")
     assert np.all(out[1] == 0.0) and np.all(lse[1] == -np.inf)
+
+
+# ----------------------------------------------------------------------------
+# the single-launch merge (FD_MERGE_FUSED): the last workgroup of each
+# (request, KV head) merges its partials inside the partial kernel
+# ----------------------------------------------------------------------------
+
+import synth
+from fdtest import Run
+
+FUSED_CASES = [  # (Hq, Hkv, lens, page, split)
+    (32, 8, (4096, 1500, 17, 0, 257), 0, 256),        # ragged, an empty request, S = 16: four splits a group
+    (32, 8, (4096, 1500, 17, 0, 257), 16, 256),
+    (8, 8, (700, 300), 0, 128),                       # MHA, S = 6: two splits a group
+    (64, 8, (9000, 2049, 1), 16, 256),                # G = 8
+    (16, 4, (5000,), 0, 64),                          # S = 79: groups of four, the last one short
+]
+
+
+def _fused_inputs(Hq, Hkv, lens, page, split, dtype="bf16", d=128, **kw):
+    base = synth.Workload("fused", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=split, N=1, page_size=page, **kw)
+    return synth.make_inputs(synth.with_lens(base, lens))
+
+
+def _counters_zero(ws):
+    import decode_attention_attn_amd as fd
+    t = ft.torch()
+    t.cuda.synchronize()
+    return bool((ws[:fd.TICKET_BYTES] == 0).all().item())
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+@pytest.mark.parametrize("Hq,Hkv,lens,page,split", FUSED_CASES)
+def test_fused_merge_matches_the_oracle(Hq, Hkv, lens, page, split, kernel):
+    import decode_attention_attn_amd as fd
+    inp = _fused_inputs(Hq, Hkv, lens, page, split)
+    r = Run(inp)
+    ws = fd.alloc_workspace(r.desc(merge="fused", kernel=kernel))
+    res = r.run(full=True, workspace=ws, merge="fused", kernel=kernel)
+    what = f"fused {kernel} Hq={Hq} Hkv={Hkv} page={page} split={split}"
+    e1, e2 = ft.check_exact(res, inp, what=what)
+    say(f"[fused] {what}: max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+    assert _counters_zero(ws), "a completed call must leave the merge counters zero"
+    for b, n in enumerate(lens):
+        if n == 0:
+            rows = slice(b * Hq, (b + 1) * Hq)
+            assert np.all(res["out"][rows] == 0.0) and np.all(res["lse"][rows] == -np.inf)
+    # the separate merge gives the same result within the bar
+    sep = r.run(full=True, merge="separate", kernel=kernel)
+    ft.assert_close(res["out"], sep["out"], inp.w.dtype, what + " vs separate out")
+    ft.assert_close(res["lse"], sep["lse"], inp.w.dtype, what + " vs separate lse")
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_fused_merge_workspace_reused_across_inputs(kernel):
+    """One workspace for a sequence of different calls: stale partials or
+    counters from a previous call would corrupt the next one."""
+    import decode_attention_attn_amd as fd
+    t = ft.torch()
+    ws = t.zeros(64 << 20, dtype=t.uint8, device="cuda")
+    cases = [(32, 8, (8000, 3000), 0, 256), (16, 4, (300, 5000, 1200), 16, 256), (32, 8, (8000, 3000), 0, 256),
+             (8, 8, (100,), 0, 64)]
+    for i, (Hq, Hkv, lens, page, split) in enumerate(cases):
+        inp = _fused_inputs(Hq, Hkv, lens, page, split)
+        if i == 2:     # the first shape again, other values
+            inp.q[:] = synth.normal(99, inp.q.shape, "bf16")
+        res = Run(inp).run(full=True, workspace=ws, merge="fused", kernel=kernel)
+        ft.check_exact(res, inp, what=f"call {i}")
+        assert _counters_zero(ws)
+
+
+def test_fused_merge_is_bitwise_repeatable():
+    inp = _fused_inputs(64, 8, (9000, 2049, 1), 16, 256)
+    r = Run(inp)
+    first = r.run(full=True, merge="fused")
+    for _ in range(4):
+        again = r.run(full=True, merge="fused")
+        assert np.array_equal(again["raw_out"], first["raw_out"]) and np.array_equal(again["lse"], first["lse"])
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_fused_merge_unified_max(kernel, page):
+    inp = _fused_inputs(32, 4, (4096, 1500), page, 256, stress_frac=0.02, stress_scale=8.0)
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = Run(inp).run(full=True, merge="fused", kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi)
+    must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may])
+    assert res["count"] == int(got.sum()) and 0 < got.sum() < got.size
+    ft.check_exact(res, inp, what=f"fused unified {kernel} page={page}")
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(4, 32, 8), (8, 32, 8), (3, 16, 4)])
+def test_fused_merge_several_query_tokens(q_len, Hq, Hkv):
+    base = synth.Workload("fusedmq", B=1, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", split=128, N=1, q_len=q_len)
+    inp = synth.make_inputs(synth.with_lens(base, (1000, 129, 3, 2 * q_len)))
+    res = Run(inp).run(full=True, merge="fused")
+    ft.check_exact(res, inp, what=f"fused q_len={q_len}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("f32", 64), ("bf16", 64)])
+def test_fused_merge_dtypes(dtype, d):
+    inp = _fused_inputs(16, 4, (3000, 1, 700), 0, 128, dtype=dtype, d=d)
+    res = Run(inp).run(full=True, merge="fused")
+    ft.check_exact(res, inp, what=f"fused {dtype} d={d}")
+
+
+@pytest.mark.parametrize("name", ["long_gqa_32k", "paged_batched_gqa"])
+def test_fused_merge_full_size(name):
+    w = synth.WORKLOADS[name]
+    say(f"[fused {name}] generating")
+    inp = synth.make_inputs(w)
+    res = Run(inp).run(full=not w.page_size, merge="fused")
+    e1, e2 = ft.check_exact(res, inp, what=f"fused {name}")
+    say(f"[fused {name}] every row: max|out err|={e1:.3e} max|lse err|={e2:.3e}")

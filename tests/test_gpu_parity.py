@@ -505,6 +505,45 @@ def test_unified_max_flags_and_fallback(kernel, page):
         ft.assert_close(res[key][agree], uo[key][agree], "bf16", f"unified {key}")
 
 
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_unified_max_whole_row_fallback(kernel, page):
+    """FD_FALLBACK_ROW: a query row with any flagged split has all of its
+    splits recomputed synchronized (the FlashDecoding++ page's whole-row
+    fallback).  Its partials are then bit for bit those of the synchronized
+    path, an unflagged row's those of the per-split fallback (which leaves it
+    alone too); the flags are the same in both modes; out and lse match the
+    oracle, and so do the partials against the oracle's whole-row fallback
+    wherever the GPU and the oracle flag a row alike."""
+    import oracle
+    base = synth.Workload("umaxrow", B=2, Hq=32, Hkv=4, d=128, dtype="bf16", split=256, N=1, page_size=page,
+                          stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, (4096, 1500)))
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -16.0, -16.0, 16.0
+    r = Run(inp)
+    row = _skip_unsupported(lambda: r.run(kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi, fallback="row"))
+    split = r.run(kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi)
+    sync = r.run(kernel=kernel)
+    assert np.array_equal(row["flags"], split["flags"]) and row["count"] == split["count"]
+    rows_flagged = row["flags"].astype(bool).any(axis=1)
+    assert rows_flagged.any() and not rows_flagged.all()
+    valid = sync["part_l"] > 0
+    for key in ("part_m", "part_l", "part_o"):
+        a, b_sync, b_split = row[key], sync[key], split[key]
+        for rr in range(a.shape[0]):
+            v = valid[rr]
+            want = b_sync[rr][v] if rows_flagged[rr] else b_split[rr][v]
+            assert np.array_equal(a[rr][v], want), (key, rr, bool(rows_flagged[rr]))
+    ft.check_exact(row, inp, what=f"whole-row fallback {kernel} page={page}")
+    uo = oracle.unified_max(oracle.problem_of(inp), inp.q, inp.k, inp.v, w.split, S, phi, lo, hi,
+                            seq_lens=inp.seq_lens, block_table=inp.block_table, whole_row=True)
+    agree = (uo["flags"].astype(bool).any(axis=1) == rows_flagged)[:, None] & (uo["part_l"] > 0)
+    for key in ("part_m", "part_l", "part_o"):
+        ft.assert_close(row[key][agree], uo[key][agree], "bf16", f"whole-row {key}")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_unified_max_all_flagged_is_bitwise_the_synchronized_path(kernel):
     base = synth.Workload("umax_all", B=2, Hq=16, Hkv=2, d=128, dtype="bf16", split=128, N=1)
@@ -760,3 +799,44 @@ def test_heuristic_split_runs_and_matches_the_oracle(B, Hq, Hkv, lens, page):
     say(f"[heuristic] split={split} S={S} (cache S_max {res['part_m'].shape[1]})")
     ft.check_exact(res, inp, what=f"heuristic split {split}")
     ft.check_partials(res, inp, split, what=f"heuristic split {split}")
+
+
+# ----------------------------------------------------------------------------
+# 8-bit caches with one scale per KV head
+# ----------------------------------------------------------------------------
+HEAD_KS = (0.011, 0.037, 0.0213, 0.05, 0.0077, 0.029, 0.017, 0.043)
+HEAD_VS = (1.9, 0.7, 1.31, 0.43, 2.2, 1.05, 0.61, 1.7)
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("Hq,Hkv,d,qdt", [(32, 8, 128, "bf16"), (16, 4, 64, "f16"), (8, 8, 128, "bf16")])
+def test_fp8_per_head_scales(kernel, Hq, Hkv, d, qdt, page):
+    inp = _fp8_workload("fp8heads", 3, Hq, Hkv, d, qdt, (1000, 1, 385), page=page, split=128,
+                        k_scales=HEAD_KS[:Hkv], v_scales=HEAD_VS[:Hkv])
+    res = Run(inp).run(kernel=kernel)
+    what = f"fp8 per-head {kernel} q={qdt} d={d} G={Hq // Hkv} page={page}"
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 128, what=what)
+
+
+def test_fp8_per_head_scales_equal_to_the_tensor_scale_are_bitwise_the_same():
+    """Per-head scales that all equal the tensor scale give the same bits as
+    the tensor scale (power-of-two scales: the products are exact either way)."""
+    a = _fp8_workload("fp8h1", 2, 32, 8, 128, "bf16", (3000, 517))
+    b = _fp8_workload("fp8h2", 2, 32, 8, 128, "bf16", (3000, 517), k_scales=(1.0 / 64,) * 8,
+                      v_scales=(1.0 / 64,) * 8)
+    assert np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    ra, rb = Run(a).run(), Run(b).run()
+    for key in ("out", "lse", "part_m", "part_l"):
+        assert np.array_equal(ra[key], rb[key]), key
+
+
+def test_fp8_per_head_scales_full_size():
+    w = synth.WORKLOADS["long_gqa_32k_fp8_head_scales"]
+    say("[long_gqa_32k_fp8_head_scales] generating")
+    inp = synth.make_inputs(w)
+    res = Run(inp).run()
+    e1, e2 = ft.check_exact(res, inp, what="fp8 per-head scales, 32k GQA")
+    ft.check_partials(res, inp, w.split, what="fp8 per-head scales, 32k GQA")
+    say(f"[long_gqa_32k_fp8_head_scales] max|out err|={e1:.3e} max|lse err|={e2:.3e}")

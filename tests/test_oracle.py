@@ -143,6 +143,70 @@ def test_brute_force_fp8_cache_with_scales():
     np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
 
 
+def test_brute_force_fp8_cache_with_per_head_scales():
+    """One scale per KV head (distinct, not powers of two): a stored value of
+    KV head h stands for stored * scale[h], and query head j reads KV head
+    j // G (the handbook's GQA map), so each query head sees its KV head's
+    scales."""
+    rng = np.random.default_rng(18)
+    B, Hq, Hkv, d, N = 2, 6, 3, 8, 7
+    ks = np.array([0.037, 0.51, 1.9])
+    vs = np.array([1.9, 0.0071, 0.33])
+    q = synth.encode(rng.standard_normal((B, Hq, d)).astype(np.float32), "bf16")
+    k = synth.encode(rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 40, "fp8")
+    v = synth.encode(rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * 40, "fp8")
+    p = oracle.problem(B, Hq, Hkv, d, "fp8", N=N, q_dtype="bf16", k_scales=ks, v_scales=vs)
+    lens = np.array([7, 4], np.int32)
+    out, lse = oracle.attention(p, q, k, v, seq_lens=lens)
+    dk = synth.decode_f64(k, "fp8") * ks[None, None, :, None]
+    dv = synth.decode_f64(v, "fp8") * vs[None, None, :, None]
+    bo, bl = brute_force(synth.decode_f64(q, "bf16"), dk, dv, None, lens=lens)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+    # the split partials merge to the same result
+    po, pm, pl = oracle.split_partials(p, q, k, v, 3, 3, seq_lens=lens)
+    mo, ml = oracle.merge(po, pm, pl)
+    np.testing.assert_allclose(mo, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml, bl, rtol=0, atol=1e-12)
+
+
+def test_equal_per_head_scales_are_the_per_tensor_scale_bitwise():
+    rng = np.random.default_rng(19)
+    B, Hq, Hkv, d, N = 2, 8, 4, 16, 30
+    c_k, c_v = 0.0377, 2.3
+    p1, q, k, v = _fp8_problem(rng, B, Hq, Hkv, d, N, c_k, c_v)
+    p2 = oracle.problem(B, Hq, Hkv, d, "fp8", N=N, q_dtype="bf16", k_scales=[c_k] * Hkv, v_scales=[c_v] * Hkv)
+    for a, b in zip(oracle.attention(p1, q, k, v), oracle.attention(p2, q, k, v)):
+        assert np.array_equal(a, b)
+
+
+def test_a_kv_heads_scale_reaches_exactly_its_query_heads():
+    """Changing the scales of KV head 1 changes the rows of query heads
+    G .. 2G - 1 and no other row."""
+    rng = np.random.default_rng(20)
+    B, Hq, Hkv, d, N = 1, 8, 4, 16, 12
+    _, q, k, v = _fp8_problem(rng, B, Hq, Hkv, d, N, 1.0, 1.0)
+    base = np.array([0.5, 0.25, 0.125, 0.75])
+    pa = oracle.problem(B, Hq, Hkv, d, "fp8", N=N, q_dtype="bf16", k_scales=base, v_scales=base)
+    moved = base.copy()
+    moved[1] = 0.3
+    pb = oracle.problem(B, Hq, Hkv, d, "fp8", N=N, q_dtype="bf16", k_scales=moved, v_scales=moved)
+    oa, la = oracle.attention(pa, q, k, v)
+    ob, lb = oracle.attention(pb, q, k, v)
+    G = Hq // Hkv
+    changed = ~np.all(oa == ob, axis=1) | (la != lb)
+    assert changed.tolist() == [G <= h < 2 * G for h in range(Hq)]
+
+
+def test_per_head_scales_must_be_positive_and_finite():
+    rng = np.random.default_rng(21)
+    _, q, k, v = _fp8_problem(rng, 1, 4, 2, 8, 5, 1.0, 1.0)
+    for bad in ([1.0, 0.0], [1.0, -2.0], [np.inf, 1.0], [np.nan, 1.0]):
+        p = oracle.problem(1, 4, 2, 8, "fp8", N=5, q_dtype="bf16", k_scales=bad)
+        with pytest.raises(ValueError):
+            oracle.attention(p, q, k, v)
+
+
 def test_fp8_cache_equals_the_fp32_cache_of_its_values_bitwise():
     """With power-of-two scales the dequantised values are exact fp32 numbers:
     the fp8 problem and the fp32 problem over those numbers agree bit for bit."""
@@ -603,6 +667,56 @@ def test_figure6_through_unified_max(golden):
         for s_idx, flag in enumerate(case["flagged_splits"]):
             part = case["scores"][2 * s_idx:2 * s_idx + 2]
             assert r["part_m"][0, s_idx] == (max(part) if flag else g["phi"])
+
+
+def test_figure6_whole_row_fallback(golden):
+    """The page's fallback recomputes the whole row: once a split of a row is
+    flagged, every split of that row takes its own maximum.  Figure 6's
+    second vector with y3 = 10 flags only the second half; its first half's
+    own maximum (6) equals phi there, so the case is taken with y2 lowered to
+    5 as well, where the first half's own maximum (5) differs from phi."""
+    g = golden("fdpp_figure6_range_check.json")
+    lo, hi = g["phi"] + g["a"], g["phi"] + g["b"]
+    for scores_, want_m in [([3.0, 6.0, 10.0, 6.0], [6.0, 10.0]), ([3.0, 5.0, 10.0, 6.0], [5.0, 10.0])]:
+        p, (q, k, v) = scalar_row_problem(scores_, [1.0, 2.0, 3.0, 4.0])
+        split_r = oracle.unified_max(p, q, k, v, split=2, S_max=2, phi=g["phi"], lo=lo, hi=hi)
+        row_r = oracle.unified_max(p, q, k, v, split=2, S_max=2, phi=g["phi"], lo=lo, hi=hi, whole_row=True)
+        assert list(row_r["flags"][0]) == [0, 1] == list(split_r["flags"][0])
+        assert list(row_r["part_m"][0]) == want_m
+        assert list(split_r["part_m"][0]) == [g["phi"], 10.0]
+        exact, lexact = oracle.attention(p, q, k, v)
+        np.testing.assert_allclose(row_r["out"], exact, atol=1e-13)
+        np.testing.assert_allclose(row_r["lse"], lexact, atol=1e-13)
+    # the first vector stays in range: nothing is recomputed, phi everywhere
+    p, (q, k, v) = scalar_row_problem([4.0, 5.0, 6.0, 7.0], [1.0, 2.0, 3.0, 4.0])
+    r = oracle.unified_max(p, q, k, v, split=2, S_max=2, phi=g["phi"], lo=lo, hi=hi, whole_row=True)
+    assert list(r["part_m"][0]) == [g["phi"], g["phi"]]
+
+
+def test_whole_row_fallback_partials_are_the_synchronized_ones_bitwise():
+    """A flagged row's partials are the synchronized split partials, bit for
+    bit; an unflagged row's are those of the per-split fallback."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, d, N = 2, 4, 2, 16, 40
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    v = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    k[0, 7, 0] *= 12.0                   # one out-of-range score for the rows of KV head 0, request 0
+    p, _ = contiguous_problem(q, k, v)
+    lens = np.array([40, 23], np.int32)
+    phi, lo, hi = -4.0, -4.0, 4.0
+    kw = dict(split=8, S_max=5, phi=phi, lo=lo, hi=hi, seq_lens=lens)
+    row_r = oracle.unified_max(p, q, k, v, whole_row=True, **kw)
+    split_r = oracle.unified_max(p, q, k, v, **kw)
+    so, sm, sl = oracle.split_partials(p, q, k, v, 8, 5, seq_lens=lens)
+    row_flagged = row_r["flags"].any(axis=1)
+    assert row_flagged.any() and not row_flagged.all()
+    assert np.array_equal(row_r["flags"], split_r["flags"])
+    for r in range(B * Hq):
+        ref = (so, sm, sl) if row_flagged[r] else (split_r["part_o"], split_r["part_m"], split_r["part_l"])
+        for got, want in zip((row_r["part_o"], row_r["part_m"], row_r["part_l"]), ref):
+            assert np.array_equal(got[r], want[r]), r
+    np.testing.assert_allclose(row_r["out"], split_r["out"], atol=1e-12)
 
 
 @pytest.mark.parametrize("offset", [-40.0, -10.0, 0.0, 7.5, 40.0])

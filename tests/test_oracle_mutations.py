@@ -39,6 +39,9 @@ MUTATIONS = [
     ("fp16 exponent bias", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
     ("fallback keeps phi", "c = s[0];", "c = phi;"),
     ("fallback partial m keeps phi", "part_m[slot] = c;", "part_m[slot] = phi;"),
+    ("whole-row fallback only recomputes the flagged split", "if (whole_row ? row_bad : bad) {", "if (bad) {"),
+    ("per-head K scale by query head", "double ks = k_scale_of(p, kvh);", "double ks = k_scale_of(p, h % p->Hkv);"),
+    ("per-head V scale of head 0", "double vs = v_scale_of(p, kvh);", "double vs = v_scale_of(p, 0);"),
 ]
 
 
