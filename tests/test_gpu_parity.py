@@ -97,12 +97,19 @@ def test_paged_batched_gqa_full():
     say("[paged_batched_gqa] generating")
     inp = synth.make_inputs(w)
     say(f"[paged_batched_gqa] {inp.k.shape[0]} pages, kv bytes {inp.kv_bytes}")
-    res = Run(inp).run()
+    r = Run(inp)
+    # the separate merge keeps the split partials in the workspace; AUTO takes
+    # the single launch for this shape (its partial rows are then internal)
+    res = r.run(merge="separate")
+    auto = r.run()
     assert np.isfinite(res["out"]).all() and np.isfinite(res["lse"]).all()
     say("[paged_batched_gqa] GPU done; oracle on every row")
-    e1, e2 = ft.check_exact(res, inp, what="paged_batched_gqa")
+    ref, lref = ft.oracle_exact(inp)
+    for what, x in (("separate", res), ("auto", auto)):
+        e1 = ft.assert_close(x["out"], ref, w.dtype, f"paged_batched_gqa {what} out")
+        e2 = ft.assert_close(x["lse"], lref, w.dtype, f"paged_batched_gqa {what} lse")
+        say(f"[paged_batched_gqa] {what}, all {len(x['lse'])} rows: max|out err|={e1:.3e} max|lse err|={e2:.3e}")
     ft.check_partials(res, inp, w.split, what="paged_batched_gqa")
-    say(f"[paged_batched_gqa] all {len(res['lse'])} rows: max|out err|={e1:.3e} max|lse err|={e2:.3e}")
 
 
 def _stress_rate_expectation(inp, c):
