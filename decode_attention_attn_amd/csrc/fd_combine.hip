@@ -164,13 +164,113 @@ hipError_t launch_shaped(const CombineParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// (launch_shaped: one workgroup of 256 threads covers all D dimensions of a
+// (request, query head); 32 to 128 dimensions per workgroup with 64 to 256
+// threads measured alike.)
+
+// One workgroup of 256 threads per (request, query row); output quad dq (dims
+// 4 dq .. 4 dq + 3) is shared by P adjacent lanes, lane ph taking splits ph,
+// ph + P, ...  Each lane requests the O quads, m and l of up to 16 of its
+// splits at once (one memory round trip: the 32k GQA shape's 128 splits are
+// 16 per lane), keeps a running max-rescaled state over them in split order,
+// and the P lanes of a quad merge by a lane butterfly.  No LDS, no barrier;
+// fixed order, so bitwise repeatable.
+template <int D>
+__global__ void __launch_bounds__(256) combine_lanes_kernel(const CombineParams p) {
+    constexpr int THREADS = 256, DQ = D / 4, P = THREADS / DQ, CH = 16;
+    const int tid = threadIdx.x, dq = tid / P, ph = tid % P;
+    const int b = blockIdx.y;
+    const size_t row = (size_t)b * p.Hq + blockIdx.x;
+    const int Smax = p.max_splits;
+    int S = Smax;
+    if (p.seq_lens) {
+        const int len = request_len(p.seq_lens, b, Smax * p.split, Smax * p.split);
+        S = (len + p.split - 1) / p.split;
+    }
+    const float *po = p.part_o + row * Smax * D + 4 * dq;
+    const float *pm = p.part_m + row * Smax, *pl = p.part_l + row * Smax;
+    float M = -INFINITY, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = ph; j0 < S; j0 += P * CH) {
+        float4 o[CH];
+        float mv[CH], lv[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int j = j0 + P * c;
+            const bool ok = j < S;
+            o[c] = ok ? *reinterpret_cast<const float4 *>(po + (size_t)j * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+            mv[c] = ok ? pm[j] : -INFINITY;
+            lv[c] = ok ? pl[j] : 0.f;
+        }
+        float mx = M;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (lv[c] > 0.f) mx = fmaxf(mx, mv[c]);
+        const float fr = M == -INFINITY ? 0.f : exp2_fast((M - mx) * kLog2e);
+        L *= fr;
+        acc.x *= fr;
+        acc.y *= fr;
+        acc.z *= fr;
+        acc.w *= fr;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (lv[c] > 0.f) {      // a split without tokens has an unwritten O row
+                const float w = lv[c] * exp2_fast((mv[c] - mx) * kLog2e);
+                L += w;
+                acc.x = fmaf(w, o[c].x, acc.x);
+                acc.y = fmaf(w, o[c].y, acc.y);
+                acc.z = fmaf(w, o[c].z, acc.z);
+                acc.w = fmaf(w, o[c].w, acc.w);
+            }
+        }
+        M = mx;
+    }
+#pragma unroll
+    for (int off = 1; off < P; off <<= 1) {
+        const float M2 = __shfl_xor(M, off), L2 = __shfl_xor(L, off);
+        const float4 a2 = make_float4(__shfl_xor(acc.x, off), __shfl_xor(acc.y, off), __shfl_xor(acc.z, off),
+                                      __shfl_xor(acc.w, off));
+        const float Mx = fmaxf(M, M2);
+        const float f1 = M == -INFINITY ? 0.f : exp2_fast((M - Mx) * kLog2e);
+        const float f2 = M2 == -INFINITY ? 0.f : exp2_fast((M2 - Mx) * kLog2e);
+        L = L * f1 + L2 * f2;
+        acc.x = acc.x * f1 + a2.x * f2;
+        acc.y = acc.y * f1 + a2.y * f2;
+        acc.z = acc.z * f1 + a2.z * f2;
+        acc.w = acc.w * f1 + a2.w * f2;
+        M = Mx;
+    }
+    if (ph == 0) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const size_t o0 = row * D + 4 * dq;
+        store_out(p.out, o0 + 0, acc.x * inv, p.out_dtype);
+        store_out(p.out, o0 + 1, acc.y * inv, p.out_dtype);
+        store_out(p.out, o0 + 2, acc.z * inv, p.out_dtype);
+        store_out(p.out, o0 + 3, acc.w * inv, p.out_dtype);
+        if (dq == 0 && p.lse) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
+    }
+}
+
+// Which combine: the lane kernel issues every load of a row at once but each
+// lane also reads the m and l of its own splits, which costs more than it
+// saves once the splits are many.  Measured on MI355X, three runs each
+// (bench.py, step time with the lane kernel against the LDS one): 4 splits
+// (tiny MHA) 9.0 against 9.5-9.95 us; 16 (Llama-2-shaped MHA) 17.65-17.72
+// against 18.40-18.58; 128 (32k GQA) 29.7-29.95 against 29.0-29.5; 128 with
+// 256 rows (B=4, N=128k) alike.
+inline bool use_lane_combine(const CombineParams &p) { return p.max_splits <= 32; }
+
 }  // namespace
 
-// One workgroup of 256 threads covers all D dimensions of a (request, query
-// head).  Measured on MI355X: 32 to 128 dimensions per workgroup with 64 to
-// 256 threads all took 4.0-4.6 us at the 32k GQA shape, the time of the
-// dependent launch rather than of the merge, so one shape serves every case.
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream) {
+    if (use_lane_combine(p)) {
+        dim3 grid(p.Hq, p.B);
+        if (p.d == 64)
+            hipLaunchKernelGGL((combine_lanes_kernel<64>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((combine_lanes_kernel<128>), grid, dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     return p.d == 64 ? launch_shaped<64, 64, 256>(p, stream) : launch_shaped<128, 128, 256>(p, stream);
 }
 
