@@ -24,6 +24,7 @@ FD_KERNEL_AUTO, FD_KERNEL_VALU, FD_KERNEL_MFMA = 0, 1, 2
 FD_MERGE_AUTO, FD_MERGE_SEPARATE, FD_MERGE_FUSED = 0, 1, 2
 FD_FALLBACK_SPLIT, FD_FALLBACK_ROW = 0, 1
 TICKET_BYTES = 65536 * 4          # FD_TICKET_BYTES: merge counters at the start of a workspace
+MAX_Q_LEN = 65536                 # FD_MAX_Q_LEN: query tokens per request
 
 DTYPES = {"f32": FD_F32, "f16": FD_F16, "bf16": FD_BF16, "fp8": FD_FP8_E4M3}
 MODES = {"sync": FD_SOFTMAX_SYNC, "unified": FD_SOFTMAX_UNIFIED_MAX}

@@ -28,8 +28,11 @@ fd_status validate_desc(const fd_decode_desc *d) {
     if (d->B < 0 || d->B > 65535 || d->Hq <= 0 || d->Hkv <= 0 || d->Hkv > 65535) return FD_ERR_INVALID_ARG;
     if (d->Hq % d->Hkv) return FD_ERR_INVALID_ARG;
     if (d->Hq / d->Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
-    if (d->q_len > kMaxRows || (int64_t)(d->q_len > 1 ? d->q_len : 1) * (d->Hq / d->Hkv) > kMaxRows)
-        return FD_ERR_UNSUPPORTED;   // a KV head's query rows must fit two 16-row matrix tiles
+    if (d->q_len > fd::kMaxQueryTokens || (int64_t)d->q_len * d->Hq > INT32_MAX) return FD_ERR_UNSUPPORTED;
+    {   // requests x query tiles index grid z; bounded for the kernel with the smaller tiles (16 rows)
+        const int64_t tok = kMaxGroup / (d->Hq / d->Hkv), q_len = d->q_len > 1 ? d->q_len : 1;
+        if ((int64_t)d->B * ((q_len + tok - 1) / tok) > fd::kMaxGridZ) return FD_ERR_UNSUPPORTED;
+    }
     if (d->d != 64 && d->d != 128) return FD_ERR_UNSUPPORTED;
     if (d->kv_dtype < FD_F32 || d->kv_dtype > FD_FP8_E4M3) return FD_ERR_INVALID_ARG;
     if (d->kv_dtype == FD_FP8_E4M3) {
@@ -82,6 +85,8 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     p.Hkv = d->Hkv;
     p.G = d->Hq / d->Hkv;
     p.q_len = d->q_len > 1 ? d->q_len : 1;
+    p.q_tiles = 1;
+    p.tile_tokens = p.q_len;
     p.R = p.q_len * p.G;
     p.d = d->d;
     p.split = d->split_size;
@@ -109,8 +114,11 @@ fd::PartialParams base_params(const fd_decode_desc *d) {
     return p;
 }
 
-// Which partial kernel runs: MFMA or VALU (FD_ERR_UNSUPPORTED if the one asked for cannot).
-fd_status pick_kernel(const fd_decode_desc *d, const fd::PartialParams &p, bool &mfma) {
+// Which partial kernel runs: MFMA or VALU (FD_ERR_UNSUPPORTED if the one asked
+// for cannot), and the query tiles of a KV head's q_len * G query rows: as few
+// tiles as the kernel's rows per workgroup allow (32 MFMA, 16 VALU), of
+// whole query tokens, balanced (40 single-head tokens: two tiles of 20).
+fd_status pick_kernel(const fd_decode_desc *d, fd::PartialParams &p, bool &mfma) {
     mfma = false;
     if (d->kernel == FD_KERNEL_MFMA) {
         if (!fd::mfma_supports(p)) return FD_ERR_UNSUPPORTED;
@@ -118,8 +126,11 @@ fd_status pick_kernel(const fd_decode_desc *d, const fd::PartialParams &p, bool 
     } else if (d->kernel == FD_KERNEL_AUTO) {
         mfma = fd::mfma_supports(p);
     }
-    if (!mfma && p.R > kMaxGroup) return FD_ERR_UNSUPPORTED;   // the VALU kernel holds up to 16 rows
-    return FD_OK;
+    const int cap = (mfma ? kMaxRows : kMaxGroup) / p.G;   // query tokens per workgroup; G <= 16
+    p.q_tiles = (p.q_len + cap - 1) / cap;
+    p.tile_tokens = (p.q_len + p.q_tiles - 1) / p.q_tiles;
+    p.R = p.tile_tokens * p.G;
+    return (int64_t)p.B * p.q_tiles <= fd::kMaxGridZ ? FD_OK : FD_ERR_UNSUPPORTED;   // validate_desc ensures it
 }
 
 bool whole_row_fallback(const fd_decode_desc *d) {
@@ -162,7 +173,7 @@ int fused_splits_per_wg(const fd::PartialParams &p) { return p.max_splits >= 8 ?
 // merge addresses them with 32-bit offsets), and one workgroup's merge fits
 // its LDS.
 bool fused_fits(const fd::PartialParams &p, bool mfma) {
-    if ((int64_t)p.B * p.Hkv > fd::kMaxTickets) return false;
+    if ((int64_t)p.B * p.q_tiles * p.Hkv > fd::kMaxTickets) return false;   // one counter per (tile, KV head)
     if ((int64_t)p.q_len * p.Hq * p.max_splits * p.d * 4 >= ((int64_t)1 << 32)) return false;
     const int64_t parts = mfma ? (p.max_splits + p.splits_per_wg - 1) / p.splits_per_wg : p.max_splits;
     return (int64_t)p.R * parts <= fd::kFusedMaxRowParts;

@@ -174,12 +174,27 @@ __device__ __forceinline__ int split_index(int x, int b, int kvh, int Hkv, int S
     return (int)(((unsigned)x + (unsigned)(b * Hkv + kvh)) % (unsigned)S);
 }
 
-// Query row rho < R of KV head kvh in request b: query token i = rho / G of
-// head kvh * G + rho % G.  Its global row (b * q_len + i) * Hq + head indexes
-// q, out and lse; its split slot indexes the partials and flags.
+// The workgroup's view of the launch parameters: grid z = b * q_tiles +
+// tile picks its request b and its row tile, query tokens i0 .. i0 +
+// tile_tokens - 1 (fewer in the last tile), whose rows become rows 0 .. R - 1.
+__device__ __forceinline__ PartialParams tile_params(const PartialParams &pk, int &b) {
+    PartialParams p = pk;
+    b = blockIdx.z;
+    p.i0 = 0;
+    if (pk.q_tiles > 1) {
+        b = (int)blockIdx.z / pk.q_tiles;
+        p.i0 = ((int)blockIdx.z - b * pk.q_tiles) * pk.tile_tokens;
+        p.R = min(pk.tile_tokens, pk.q_len - p.i0) * pk.G;
+    }
+    return p;
+}
+
+// Query row rho < R of KV head kvh in request b: query token i = i0 + rho / G
+// of head kvh * G + rho % G.  Its global row (b * q_len + i) * Hq + head
+// indexes q, out and lse; its split slot indexes the partials and flags.
 __device__ __forceinline__ size_t query_row(const PartialParams &p, int b, int kvh, int rho) {
-    const int i = rho / p.G, g = rho - i * p.G;
-    return ((size_t)b * p.q_len + i) * p.Hq + (size_t)kvh * p.G + g;
+    const int t = rho / p.G, g = rho - t * p.G;
+    return ((size_t)b * p.q_len + p.i0 + t) * p.Hq + (size_t)kvh * p.G + g;
 }
 
 __device__ __forceinline__ size_t row_slot(const PartialParams &p, int b, int kvh, int rho, int s) {
@@ -189,8 +204,16 @@ __device__ __forceinline__ size_t row_slot(const PartialParams &p, int b, int kv
 // Causal limit of query row rho inside the split ending at t1: query token i
 // sits at position len - q_len + i and sees the tokens up to it.
 __device__ __forceinline__ int row_limit(const PartialParams &p, int len, int t1, int rho) {
-    const int lim = len - p.q_len + rho / p.G + 1;
+    const int lim = len - p.q_len + p.i0 + rho / p.G + 1;
     return lim < t1 ? lim : t1;
+}
+
+// Tokens of a request of len tokens that some row of the workgroup's tile
+// sees: those before its last query token's causal limit.  The splits past
+// it are empty for the tile (all len of them when rows are not tiled).
+__device__ __forceinline__ int tile_len(const PartialParams &p, int len) {
+    const int lim = len - p.q_len + p.i0 + p.R / p.G;
+    return lim < 0 ? 0 : lim;
 }
 
 // Whole-row fallback, second pass: the query rows (bit rho) of KV head kvh
@@ -202,8 +225,7 @@ __device__ __forceinline__ uint32_t rows_flagged_in_request(const PartialParams 
     uint32_t m = 0;
     for (int idx = lane; idx < p.R * nsplit; idx += 64) {
         const int rho = idx / nsplit, s = idx - rho * nsplit;
-        const size_t slot = (((size_t)b * p.q_len + rho / p.G) * p.Hq + (size_t)kvh * p.G + rho % p.G) * p.max_splits + s;
-        if (p.flags[slot]) m |= 1u << rho;
+        if (p.flags[row_slot(p, b, kvh, rho, s)]) m |= 1u << rho;
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) m |= (uint32_t)__shfl_xor((int)m, off);

@@ -10,7 +10,9 @@ namespace fd {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxGroup = 16;       // query heads per KV head
-constexpr int kMaxRows = 32;        // query rows per KV head, q_len * G (MFMA kernel; VALU: 16)
+constexpr int kMaxRows = 32;        // query rows per workgroup (MFMA kernel; VALU: kMaxGroup)
+constexpr int kMaxQueryTokens = 65536;
+constexpr int kMaxGridZ = 65535;    // requests x row tiles
 constexpr int kMaxSplits = 4096;    // the combine stages m and l of every split in LDS
 constexpr int kMaxSplitSize = 1 << 20;
 // single-launch merge: query rows x partials that one workgroup merges
@@ -39,7 +41,12 @@ struct PartialParams {
     int32_t *fallback_count;    // [1] or nullptr
     int32_t B, Hq, Hkv, G, d;
     int32_t q_len;              // query tokens per request (causal)
-    int32_t R;                  // query rows per KV head: q_len * G (<= 16)
+    // A KV head's q_len * G query rows go in query tiles of tile_tokens whole
+    // query tokens (the last tile may be shorter); grid z = b * q_tiles + tile.
+    int32_t q_tiles;
+    int32_t tile_tokens;
+    int32_t R;                  // query rows of a workgroup: host, a full tile's; device, its own tile's
+    int32_t i0;                 // device: first query token of the workgroup's tile
     int32_t kv_capacity;        // contiguous: tokens per request row; paged: max_blocks * page
     int32_t page_size;          // 0 = contiguous
     int32_t max_blocks;

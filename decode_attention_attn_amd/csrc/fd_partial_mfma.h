@@ -661,17 +661,19 @@ __device__ __forceinline__ void head_scales(const PartialParams &p, int kvh, flo
 
 template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
-partial_mfma_kernel(const PartialParams p) {
+partial_mfma_kernel(const PartialParams pk) {
     using C = MCfg<D, GMAX, WAVES>;
     static_assert(WAVES == 1 || WAVES == 2, "the epilogue merges at most two waves");
     static_assert(sizeof(MSmem<D, GMAX, WAVES>) <= 65536, "LDS budget of one workgroup");
     __shared__ MSmem<D, GMAX, WAVES> sm;
-    const int kvh = kv_head_of(p, blockIdx.y), b = blockIdx.z;
-    const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
-    const int R = p.R;                               // query rows of this KV head
+    int b;
+    const PartialParams p = tile_params(pk, b);
+    const int kvh = kv_head_of(p, blockIdx.y);
+    const int s = split_index(blockIdx.x, blockIdx.z, kvh, p.Hkv, p.max_splits);
+    const int R = p.R;                               // query rows of this workgroup
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
     const int t0 = s * p.split;
-    const int t1 = min(t0 + p.split, len);
+    const int t1 = min(t0 + p.split, tile_len(p, len));
 
     if (t0 >= t1) {
         if (threadIdx.x < R && !p.recompute_rows) {
@@ -821,18 +823,21 @@ __device__ void store_group_partial(const PartialParams &p, const MState<D, GMAX
 // four waves per CU, the 32k GQA shape's, holds only one wave per SIMD).
 template <int T, int D, int GMAX, int SW, bool PAGED, bool UNI>
 __global__ void __launch_bounds__(64 * SW) __attribute__((amdgpu_waves_per_eu(2)))
-fused_mfma_kernel(const PartialParams p) {
+fused_mfma_kernel(const PartialParams pk) {
     using C = MCfg<D, GMAX, 1>;
     constexpr int NT = row_tiles(GMAX);
     static_assert(sizeof(FSmem<D, GMAX, SW>) <= 65536, "LDS budget of one workgroup");
     __shared__ FSmem<D, GMAX, SW> sm;
+    int b;
+    const PartialParams p = tile_params(pk, b);
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's split in the group
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int x = split_index(blockIdx.x, b, kvh, p.Hkv, gridDim.x);        // the group's index in the head
+    const int kvh = blockIdx.y;
+    const int x = split_index(blockIdx.x, blockIdx.z, kvh, p.Hkv, gridDim.x);   // the group's index in the head
     const int s = x * SW + w;                                                // this wave's split
     const int R = p.R, lane = threadIdx.x & 63;
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
-    const int nb = (len + SW * p.split - 1) / (SW * p.split);               // groups holding tokens
+    const int tl = tile_len(p, len);                                         // tokens the tile's rows see
+    const int nb = (tl + SW * p.split - 1) / (SW * p.split);                // groups holding tokens
 
     if (x >= nb) {   // none of the group's splits holds a token
         if (p.flags && lane < R && s < p.max_splits) p.flags[row_slot(p, b, kvh, lane, s)] = 0;
@@ -840,7 +845,7 @@ fused_mfma_kernel(const PartialParams p) {
         return;
     }
 
-    const int t0 = s * p.split, t1 = min(t0 + p.split, len);   // t0 >= t1: a split past the request's end
+    const int t0 = s * p.split, t1 = min(t0 + p.split, tl);   // t0 >= t1: a split past the tile's tokens
     float sc, vmul;
     head_scales<T>(p, kvh, sc, vmul);
     uint4 qop[NT][C::KS];
@@ -896,13 +901,13 @@ fused_mfma_kernel(const PartialParams p) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) store_group_partial<T, D, GMAX, SW>(p, st[rt], lsum[rt], sm, rt, b, kvh, x, vmul);
     }
-    if (arrive_last(&p.tickets[(size_t)b * p.Hkv + kvh], nb, &sm.ticket))
+    if (arrive_last(&p.tickets[(size_t)blockIdx.z * p.Hkv + kvh], nb, &sm.ticket))
         merge_rows<D, 64 * SW>(p, b, kvh, nb, sm.merge);
 }
 
 template <int T, int D, int GMAX, int SW, bool PAGED>
 hipError_t launch_fused_shaped(const PartialParams &p, hipStream_t stream) {
-    dim3 grid((p.max_splits + SW - 1) / SW, p.Hkv, p.B);
+    dim3 grid((p.max_splits + SW - 1) / SW, p.Hkv, p.B * p.q_tiles);
     if (p.unified)
         hipLaunchKernelGGL((fused_mfma_kernel<T, D, GMAX, SW, PAGED, true>), grid, dim3(64 * SW), 0, stream, p);
     else
@@ -929,14 +934,14 @@ hipError_t launch_fused(const PartialParams &p, hipStream_t stream) {
 // takes one with more rows.
 template <int T>
 inline int launch_waves(const PartialParams &p) {
-    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B;
+    const int64_t wgs = (int64_t)p.max_splits * p.Hkv * p.B * p.q_tiles;
     if (wgs < 4 * (int64_t)p.num_cus) return 2;
     return (!f8_of(T) || p.R > 4) ? 1 : 2;
 }
 
 template <int T, int D, int GMAX, int WAVES, bool PAGED>
 hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
-    dim3 grid(p.max_splits, p.Hkv, p.B);
+    dim3 grid(p.max_splits, p.Hkv, p.B * p.q_tiles);
     if (p.unified)
         hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, true>), grid, dim3(64 * WAVES), 0, stream,
                            p);

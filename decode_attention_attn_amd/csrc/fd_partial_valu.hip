@@ -234,19 +234,22 @@ union VSmem {
 // FUSED: the single-launch merge (one split per workgroup; the last workgroup
 // of a (request, KV head) merges its splits into out and lse, fd_merge.h).
 template <int DT, int D, int GMAX, bool PAGED, bool FUSED>
-__global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
+__global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams pk) {
     using C = Cfg<DT, D, GMAX>;
     constexpr int E = C::E;
     __shared__ VSmem<D, GMAX> vsm;
     __shared__ int ticket;
     Smem<D, GMAX> &sm = vsm.st;
 
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int s = split_index(blockIdx.x, b, kvh, p.Hkv, p.max_splits);
-    const int G = p.R;                               // query rows of this KV head
+    int b;
+    const PartialParams p = tile_params(pk, b);
+    const int kvh = blockIdx.y;
+    const int s = split_index(blockIdx.x, blockIdx.z, kvh, p.Hkv, p.max_splits);
+    const int G = p.R;                               // query rows of this workgroup
     const int len = request_len(p.seq_lens, b, p.kv_capacity, p.max_splits * p.split);
+    const int tl = tile_len(p, len);                 // tokens the tile's rows see
     const int t0 = s * p.split;
-    const int t1 = min(t0 + p.split, len);
+    const int t1 = min(t0 + p.split, tl);
 
     if (t0 >= t1) {   // empty split: nothing to read
         if (threadIdx.x < G && !p.recompute_rows) {
@@ -257,7 +260,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
             }
             if (p.flags) p.flags[slot] = 0;
         }
-        if (FUSED && len <= 0 && s == 0) write_empty_rows<D>(p, b, kvh, kThreads);
+        if (FUSED && tl <= 0 && s == 0) write_empty_rows<D>(p, b, kvh, kThreads);
         return;
     }
     // whole-row fallback, second pass: only rows flagged in some split of the request
@@ -332,15 +335,16 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     if (p.flags && threadIdx.x < G && !p.recompute_rows)
         p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
     if constexpr (FUSED) {
-        const int nb = (len + p.split - 1) / p.split;       // splits holding tokens
+        const int nb = (tl + p.split - 1) / p.split;        // splits holding tokens
         __syncthreads();                                     // the merge area overlays the epilogue's
-        if (arrive_last(&p.tickets[(size_t)b * p.Hkv + kvh], nb, &ticket)) merge_rows<D, kThreads>(p, b, kvh, nb, vsm.merge);
+        if (arrive_last(&p.tickets[(size_t)blockIdx.z * p.Hkv + kvh], nb, &ticket))
+            merge_rows<D, kThreads>(p, b, kvh, nb, vsm.merge);
     }
 }
 
 template <int DT, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
-    dim3 grid(p.max_splits, p.Hkv, p.B);
+    dim3 grid(p.max_splits, p.Hkv, p.B * p.q_tiles);
     if (p.tickets)
         hipLaunchKernelGGL((partial_valu_kernel<DT, D, GMAX, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
     else

@@ -35,9 +35,18 @@
  *    FlashAttention forward kernel, page "FlashAttention and inference
  *    kernels", section "FlashAttention: tiling plus online softmax").  Every
  *    per-head shape below is per query row: out [B, q_len, Hq, d], lse, m, l
- *    and flags [B, q_len, Hq, ...].  q_len * (Hq / Hkv) <= 32; more than 16 rows
- *    per KV head need the MFMA kernel (the VALU kernel reports them
- *    FD_ERR_UNSUPPORTED).
+ *    and flags [B, q_len, Hq, ...].  q_len <= FD_MAX_Q_LEN and
+ *    q_len * Hq < 2^31.  A workgroup holds up to 32 query rows of one KV
+ *    head (MFMA kernel; VALU kernel: 16): a KV head with more rows, e.g. a
+ *    prefill chunk, is processed in query tiles of whole query tokens, each
+ *    tile its own set of split workgroups that reads only the cache tokens
+ *    its rows can see.  The handbook page's forward kernel likewise gives
+ *    each block of query rows its own pass over K and V (section "A working
+ *    FlashAttention forward kernel"), and the tiled causal algorithm skips
+ *    the tiles past the diagonal (section "How FlashAttention evolved").
+ *    B * ceil(q_len / floor(16 / (Hq / Hkv))) must stay <= 65535 (the tile
+ *    count of the VALU kernel, the larger of the two), else
+ *    FD_ERR_UNSUPPORTED.
  *  - 8-bit caches (FD_FP8_E4M3, OCP FP8 E4M3: bias 7, no infinities, largest
  *    finite 448, S.1111.111 = NaN) stand for stored * k_scale and
  *    stored * v_scale, with one scale per tensor or one per KV head
@@ -244,6 +253,9 @@ fd_status fd_decode_attn_paged_noalloc(const fd_decode_desc *desc, const void *q
                                        const int32_t *block_table, int32_t max_blocks_per_seq,
                                        const int32_t *seq_lens, void *out, float *lse, uint8_t *flags,
                                        int32_t *fallback_count, void *stream);
+
+/* Most query tokens per request (desc->q_len). */
+#define FD_MAX_Q_LEN 65536
 
 /* Bytes of the merge counters at the start of a workspace. */
 #define FD_TICKET_BYTES (65536u * 4u)

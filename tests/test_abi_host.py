@@ -28,6 +28,20 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_header_constants_match_the_binding():
+    text = HEADER.read_text()
+
+    def define(name):
+        expr = re.search(rf"#define {name} (.+)", text).group(1)
+        expr = re.sub(r"(\d+)u\b", r"\1", expr)
+        assert re.fullmatch(r"[\d\s()*<+]+", expr), expr     # integers, *, << only
+        return eval(expr)
+
+    assert define("FD_TICKET_BYTES") == fd.TICKET_BYTES
+    assert define("FD_MAX_Q_LEN") == fd.MAX_Q_LEN
+    assert define("FD_NOALLOC_SCRATCH_BYTES") == fd.NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings():
     assert fd.fd_status_string(fd.FD_OK) == "FD_OK"
     assert fd.fd_status_string(fd.FD_ERR_WORKSPACE_TOO_SMALL) == "FD_ERR_WORKSPACE_TOO_SMALL"
@@ -201,14 +215,26 @@ def test_fp8_descriptor_validation():
 
 
 def test_multi_query_descriptor_validation():
-    """q_len * (Hq / Hkv) query rows of a KV head must fit two 16-row tiles
-    (INVALID_ARG below only says validation passed: the test hands no tensors);
-    more than 16 rows need the MFMA kernel."""
-    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=4)) == fd.FD_ERR_INVALID_ARG
-    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=8)) == fd.FD_ERR_INVALID_ARG
-    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=9)) == fd.FD_ERR_UNSUPPORTED
-    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=32)) == fd.FD_ERR_INVALID_ARG
-    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=33)) == fd.FD_ERR_UNSUPPORTED
+    """Any q_len up to FD_MAX_Q_LEN with q_len * Hq < 2^31 is valid (rows beyond
+    a workgroup's go in query tiles; INVALID_ARG below only says validation
+    passed: the test hands no tensors)."""
+    ok = fd.FD_ERR_INVALID_ARG
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=4)) == ok
+    assert _partial_status(fd.make_desc(1, 32, 8, 128, "bf16", max_splits=4, q_len=9)) == ok
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=33)) == ok
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4, q_len=fd.MAX_Q_LEN)) == ok
+    assert _partial_status(fd.make_desc(1, 8, 8, 128, "bf16", max_splits=4,
+                                        q_len=fd.MAX_Q_LEN + 1)) == fd.FD_ERR_UNSUPPORTED
+    # q_len * Hq = 2^31 query rows per request
+    assert _partial_status(fd.make_desc(1, 32768, 2048, 128, "bf16", max_splits=4,
+                                        q_len=fd.MAX_Q_LEN)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(1, 32767 * 16, 32767, 128, "bf16", max_splits=4,
+                                        q_len=4096)) == ok
+    # requests x query tiles of 16 rows (one token each for a group of 16) <= 65535
+    assert _partial_status(fd.make_desc(1023, 16, 1, 64, "bf16", max_splits=4, q_len=64)) == ok
+    assert _partial_status(fd.make_desc(1024, 16, 1, 64, "bf16", max_splits=4, q_len=64)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(1, 8, 1, 64, "bf16", max_splits=4, q_len=65535 * 2)) == fd.FD_ERR_UNSUPPORTED
+    assert _partial_status(fd.make_desc(2, 8, 1, 64, "bf16", max_splits=4, q_len=65534)) == ok
     one = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4)
     zero = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=0)
     four = fd.make_desc(2, 8, 8, 128, "bf16", max_splits=4, q_len=4)

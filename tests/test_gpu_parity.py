@@ -722,17 +722,93 @@ def test_multi_query_causal(kernel, dtype, Hq, Hkv, q_len, d, page):
         assert np.all(res["out"][r0:r0 + Hq] == 0.0) and np.all(res["lse"][r0:r0 + Hq] == -np.inf)
 
 
-def test_more_than_16_rows_need_the_mfma_kernel():
-    import decode_attention_attn_amd as fd
-    base = synth.Workload("mq32", B=1, Hq=64, Hkv=8, d=128, dtype="bf16", split=128, N=1, q_len=4)
-    inp = synth.make_inputs(synth.with_lens(base, (700,)))
-    with pytest.raises(fd.FdError) as e:
-        Run(inp).run(kernel="valu")
-    assert e.value.status == fd.FD_ERR_UNSUPPORTED
-    f32 = synth.make_inputs(synth.with_lens(dataclasses.replace(base, dtype="f32"), (700,)))
-    with pytest.raises(fd.FdError) as e:                # auto: no kernel for 32 fp32 rows
-        Run(f32).run()
-    assert e.value.status == fd.FD_ERR_UNSUPPORTED
+# ----------------------------------------------------------------------------
+# query tiles: more query rows per KV head than a workgroup holds (32 MFMA,
+# 16 VALU), e.g. a prefill chunk or a whole prompt; the rows go in tiles of
+# whole query tokens, each reading only the cache tokens its rows can see
+# ----------------------------------------------------------------------------
+QT_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d): tiles of the kernel's rows
+    ("mfma", "bf16", 32, 8, 20, 128),     # G=4, 80 rows: tiles of 7, 7, 6 tokens
+    ("mfma", "f16", 8, 8, 100, 128),      # G=1, 100 rows: 4 tiles of 25
+    ("mfma", "fp8", 64, 8, 9, 128),       # G=8, 72 rows: 3 tiles of 3
+    ("mfma", "bf16", 16, 4, 70, 64),      # G=4, 280 rows: 9 tiles (8 tokens, the last 6)
+    ("valu", "f32", 16, 8, 20, 128),      # G=2, 40 rows: tiles of 7, 7, 6
+    ("valu", "bf16", 8, 8, 40, 64),       # G=1: tiles of 14, 14, 12
+    ("valu", "fp8", 32, 8, 6, 128),       # G=4: 2 tiles of 3
+    ("auto", "f32", 64, 8, 4, 128),       # G=8, 32 rows: 2 VALU tiles of 2 tokens
+]
+
+
+def _tile_inputs(dtype, Hq, Hkv, q_len, d, page=0, **kw):
+    extra = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if dtype == "fp8" else {}
+    extra.update(kw)
+    base = synth.Workload("qt", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=128, N=1, page_size=page,
+                          q_len=q_len, **extra)
+    # a request as long as its query tokens (a whole prompt), shorter ones (the
+    # early tiles see nothing), and longer ones across split boundaries
+    return synth.make_inputs(synth.with_lens(base, (1000, 3, q_len, 2 * q_len + 129, 257)))
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", QT_CASES)
+def test_query_tiles(kernel, dtype, Hq, Hkv, q_len, d, page):
+    inp = _tile_inputs(dtype, Hq, Hkv, q_len, d, page)
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, merge="separate"))
+    what = f"tiles q_len={q_len} {kernel} {dtype} d={d} G={Hq // Hkv} page={page}"
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 128, what=what)
+    # the request of 3 tokens: its query tokens before the last 3 see nothing
+    r0 = (1 * q_len) * Hq
+    n_blind = (q_len - 3) * Hq
+    assert np.all(res["out"][r0:r0 + n_blind] == 0.0) and np.all(res["lse"][r0:r0 + n_blind] == -np.inf)
+
+
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", [QT_CASES[0], QT_CASES[3], QT_CASES[4], QT_CASES[5]])
+def test_query_tiles_single_launch(kernel, dtype, Hq, Hkv, q_len, d):
+    """The single-launch merge with one counter per (request, tile, KV head)."""
+    inp = _tile_inputs(dtype, Hq, Hkv, q_len, d)
+    for _ in range(2):                                  # counters left zero for the next call
+        res = Run(inp).run(kernel=kernel, full=True, merge="fused")
+        ft.check_exact(res, inp, what=f"tiles fused q_len={q_len} {kernel} {dtype}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("fallback", ["split", "row"])
+def test_query_tiles_unified_max(kernel, fallback):
+    inp = _tile_inputs("bf16", 32, 8, 12, 128, stress_frac=0.02, stress_scale=8.0)
+    w = inp.w
+    S = -(-w.N // w.split)
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, mode="unified", phi=phi, lo=lo, hi=hi,
+                                                 fallback=fallback))
+    must, may = ft.flag_bounds(inp, w.split, S, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may])
+    assert 0 < got.sum() < got.size
+    ft.check_exact(res, inp, what=f"tiles unified {kernel} {fallback}")
+
+
+def test_query_tiles_match_untiled_rows_bitwise():
+    """A tile's rows are computed as they are without tiles: the VALU kernel
+    (16 rows per workgroup) on 32 rows in two tiles gives the bits of the
+    same rows run as two calls of 16 rows each (the last q_len / 2 tokens,
+    and the first q_len / 2 at a request length shortened by q_len / 2)."""
+    w = synth.Workload("qtb", B=1, Hq=8, Hkv=2, d=128, dtype="bf16", split=128, N=1, q_len=8)
+    inp = synth.make_inputs(synth.with_lens(w, (900, 300)))
+    res = Run(inp).run(kernel="valu")
+    w = inp.w
+    half = w.q_len // 2
+    for part, (i0, cut) in enumerate(((0, half), (half, 0))):
+        lens = inp.seq_lens - cut
+        w1 = dataclasses.replace(w, q_len=half, fixed_lens=tuple(int(x) for x in lens), name="qtb1")
+        inp1 = synth.Inputs(w1, np.ascontiguousarray(inp.q[:, i0:i0 + half]), inp.k, inp.v,
+                            lens.astype(np.int32))
+        r1 = Run(inp1).run(kernel="valu")
+        for b in range(w.B):
+            r = slice((b * w.q_len + i0) * w.Hq, (b * w.q_len + i0 + half) * w.Hq)
+            r_1 = slice(b * half * w.Hq, (b + 1) * half * w.Hq)
+            assert np.array_equal(res["out"][r], r1["out"][r_1]), (part, b)
+            assert np.array_equal(res["lse"][r], r1["lse"][r_1]), (part, b)
 
 
 @pytest.mark.parametrize("q_len,Hq", [(4, 16), (4, 64)])

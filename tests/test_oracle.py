@@ -277,6 +277,49 @@ def test_multi_query_rows_are_single_queries_with_causal_lengths_bitwise():
     assert np.all(out[r:r + Hq] == 0.0) and np.all(lse[r:r + Hq] == -np.inf)
 
 
+def test_prefill_equals_torch_causal_attention():
+    """Every token of the request a query (q_len = len): the handbook's causal
+    FlashAttention forward (page "FlashAttention and inference kernels",
+    section "How FlashAttention evolved", the causal mask), which torch's
+    scaled_dot_product_attention with is_causal computes (fp64, CPU); GQA by
+    repeating each KV head for its group of consecutive query heads."""
+    import torch
+    rng = np.random.default_rng(31)
+    B, L, Hq, Hkv, d = 2, 70, 8, 2, 16
+    p, q, k, v, lens = _multi_query_case(rng, B, L, Hq, Hkv, d, L, (L, L))
+    out, lse = oracle.attention(p, q, k, v, seq_lens=lens)
+    G = Hq // Hkv
+    tq = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)              # [B, Hq, L, d]
+    tk = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    tv = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    ref = ref.permute(0, 2, 1, 3).reshape(B * L * Hq, d).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_prefill_chunk_rows_equal_the_full_prefill_rows_bitwise():
+    """A chunk of the last C query tokens (q_len = C) gives the rows of those
+    tokens in a call with all L query tokens, bit for bit: the same keys per
+    row, whatever the chunk's length (request 1 is shorter than L, so its
+    first query tokens see nothing in the longer call)."""
+    rng = np.random.default_rng(32)
+    B, L, Hq, Hkv, d = 2, 45, 4, 4, 8
+    pf, q, k, v, lens = _multi_query_case(rng, B, L, Hq, Hkv, d, L, (L, 30))
+    full, lfull = oracle.attention(pf, q, k, v, seq_lens=lens)
+    for C in (1, 7, 30):
+        pc = oracle.problem(B, Hq, Hkv, d, "f32", N=L, q_len=C)
+        qc = np.ascontiguousarray(q[:, L - C:])
+        out, lse = oracle.attention(pc, qc, k, v, seq_lens=lens)
+        for b in range(B):
+            for i in range(C):
+                # chunk query i and full query L - C + i both sit at position len - C + i
+                rf = (b * L + L - C + i) * Hq
+                rc = (b * C + i) * Hq
+                assert np.array_equal(out[rc:rc + Hq], full[rf:rf + Hq]), (C, b, i)
+                assert np.array_equal(lse[rc:rc + Hq], lfull[rf:rf + Hq]), (C, b, i)
+
+
 # ----------------------------------------------------------------------------
 # the handbook's worked online-softmax exercise
 # ----------------------------------------------------------------------------
