@@ -39,6 +39,8 @@ if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD public spec
+MFMA_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 / f16 matrix peak (the 16-bit and 8-bit caches' path)
+VALU_F32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector peak (the fp32 cache's VALU kernel)
 MALL_BYTES = 256 * 2 ** 20        # Infinity Cache
 PARTIAL_KERNEL = "partial"        # substring of the split-partial kernels' names
 COPY_BYTES = 256 * 2 ** 20        # calibration copy: reads and writes this many bytes
@@ -77,8 +79,25 @@ def algorithmic_bytes(inp):
     table = 0
     if w.page_size:
         table = int(((inp.seq_lens.astype(np.int64) + w.page_size - 1) // w.page_size).sum()) * 4
+    # flops: q.k and p.v, 2 d each, for every (query row, cache token it sees)
+    lens = inp.seq_lens.astype(np.int64)
+    seen = np.clip(lens[:, None] - w.q_len + np.arange(w.q_len, dtype=np.int64)[None, :] + 1, 0, lens[:, None])
+    flops = 4 * w.d * w.Hq * int(seen.sum())
     return dict(kv=kv, q=q, out=out, table=table, partial=kv + q + table, step=kv + q + out + table,
-                units=int(inp.seq_lens.astype(np.int64).sum()) * w.Hkv, per_unit=2 * w.d * eb)
+                units=int(lens.sum()) * w.Hkv, per_unit=2 * w.d * eb, flops=flops)
+
+
+def roofline_bound(w, kernel, alg):
+    """'hbm' or 'mfma'/'valu' for the partial kernel, with the compute peak of
+    the kernel that runs it: whichever of the algorithmic bytes at the HBM
+    peak and the algorithmic flops at the compute peak takes longer."""
+    matrix = w.dtype in ("f16", "bf16", "fp8") and kernel != "valu"
+    peak = MFMA_PEAK_TFLOPS if matrix else VALU_F32_PEAK_TFLOPS
+    compute_s = alg["flops"] / (peak * 1e12)
+    memory_s = alg["partial"] / (HBM_PEAK_GBPS * 1e9)
+    if compute_s <= memory_s:
+        return "hbm", HBM_PEAK_GBPS
+    return ("mfma" if matrix else "valu"), peak
 
 
 # ----------------------------------------------------------------------------
@@ -446,7 +465,11 @@ def main():
     else:   # auto: whichever the library took
         keys = [["fused"], [PARTIAL_KERNEL, "combine"]]
     traffic = traffic_from_profile(w.name, keys, run_settings(args))
-    achieved = alg["partial"] / part_s / 1e9
+    bound, peak = roofline_bound(w, args.kernel, alg)
+    if bound == "hbm":
+        achieved, unit = alg["partial"] / part_s / 1e9, "GB/s"
+    else:
+        achieved, unit = alg["flops"] / part_s / 1e12, "TFLOP/s"
     line = {
         "metric": "decode-attn us/step and achieved HBM TB/s (% of MI355X peak), N=32k GQA",
         "value": alg["step"] / step_s / 1e12,
@@ -469,10 +492,11 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
         "kernels_us": {"partial": float(np.mean(g["part_us"])), "combine": float(np.mean(g["comb_us"])),
                        "timing": "HIP events around K back-to-back launches of each kernel"},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+        "roofline": {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg["partial"], "per_unit_bytes": alg["per_unit"],
-                     "units_per_launch": alg["units"]},
+                     "units_per_launch": alg["units"], "algorithmic_flops_per_launch": alg["flops"],
+                     "hbm_gbps": alg["partial"] / part_s / 1e9, "tflops": alg["flops"] / part_s / 1e12},
         "parity": parity,
         "device": g["device"],
     }

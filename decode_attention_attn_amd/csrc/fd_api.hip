@@ -310,14 +310,23 @@ fd_status run_full(const fd_decode_desc *desc, fd::PartialParams &p, void *works
     bool mfma = false;
     fd_status st = pick_kernel(desc, p, mfma);
     if (st != FD_OK) return st;
+    p.out = out;
+    p.lse = lse;
+    p.out_dtype = desc->out_dtype;
+    if (desc->merge == FD_MERGE_AUTO && p.max_splits == 1 && !p.unified) {
+        // one split per row: its partial is the result, written by the partial
+        // kernel itself (no partials, no merge: the Flash-Decoding page's
+        // "Production Implementation Guidelines" need no split once the batch
+        // and heads fill the GPU).  Synchronized softmax only: unified max,
+        // with its recompute passes, keeps the partials and the merge.
+        p.direct = 1;
+        return run_partial(desc, p, s);
+    }
     p.splits_per_wg = fused_splits_per_wg(p);
     const bool fits = fused_possible(desc, p, mfma);
     if (desc->merge == FD_MERGE_FUSED && !fits) return FD_ERR_UNSUPPORTED;
     if (fits && fused_wanted(desc, p, mfma)) {
         p.tickets = reinterpret_cast<int32_t *>(ws);
-        p.out = out;
-        p.lse = lse;
-        p.out_dtype = desc->out_dtype;
         const hipError_t e = mfma ? fd::launch_partial_mfma(p, s) : fd::launch_partial_valu(p, s);
         return e == hipSuccess ? FD_OK : FD_ERR_HIP;
     }

@@ -174,18 +174,21 @@ __device__ __forceinline__ int split_index(int x, int b, int kvh, int Hkv, int S
     return (int)(((unsigned)x + (unsigned)(b * Hkv + kvh)) % (unsigned)S);
 }
 
-// The workgroup's view of the launch parameters: grid z = b * q_tiles +
-// tile picks its request b and its row tile, query tokens i0 .. i0 +
-// tile_tokens - 1 (fewer in the last tile), whose rows become rows 0 .. R - 1.
+// The workgroup's view of the launch parameters: grid z = b * q_tiles + j
+// picks its request b and its query tile, tokens i0 .. i0 + tile_tokens - 1
+// (fewer in the last tile), whose rows become rows 0 .. R - 1.  The tiles go
+// in reverse (j = 0 is the last tile): later query tokens see more of the
+// cache, so the longest workgroups start first and the short ones fill the
+// tail.
+// Branch-free, so that the compiler issues every parameter load at once (a
+// branch on q_tiles delayed the other loads behind it by a load round trip).
 __device__ __forceinline__ PartialParams tile_params(const PartialParams &pk, int &b) {
     PartialParams p = pk;
-    b = blockIdx.z;
-    p.i0 = 0;
-    if (pk.q_tiles > 1) {
-        b = (int)blockIdx.z / pk.q_tiles;
-        p.i0 = ((int)blockIdx.z - b * pk.q_tiles) * pk.tile_tokens;
-        p.R = min(pk.tile_tokens, pk.q_len - p.i0) * pk.G;
-    }
+    const unsigned z = blockIdx.z, nt = (unsigned)pk.q_tiles;
+    b = (int)(z / nt);
+    const int tile = (int)(nt - 1u - (z - (unsigned)b * nt));
+    p.i0 = tile * pk.tile_tokens;
+    p.R = min(pk.tile_tokens, pk.q_len - p.i0) * pk.G;
     return p;
 }
 
@@ -229,7 +232,7 @@ __device__ __forceinline__ uint32_t rows_flagged_in_request(const PartialParams 
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) m |= (uint32_t)__shfl_xor((int)m, off);
-    return m;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)m);   // uniform: a scalar register
 }
 
 // Number of tokens of request b that the kernels read.

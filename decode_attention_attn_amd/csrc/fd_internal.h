@@ -41,12 +41,7 @@ struct PartialParams {
     int32_t *fallback_count;    // [1] or nullptr
     int32_t B, Hq, Hkv, G, d;
     int32_t q_len;              // query tokens per request (causal)
-    // A KV head's q_len * G query rows go in query tiles of tile_tokens whole
-    // query tokens (the last tile may be shorter); grid z = b * q_tiles + tile.
-    int32_t q_tiles;
-    int32_t tile_tokens;
     int32_t R;                  // query rows of a workgroup: host, a full tile's; device, its own tile's
-    int32_t i0;                 // device: first query token of the workgroup's tile
     int32_t kv_capacity;        // contiguous: tokens per request row; paged: max_blocks * page
     int32_t page_size;          // 0 = contiguous
     int32_t max_blocks;
@@ -68,11 +63,20 @@ struct PartialParams {
     float *lse;                 // [B, q_len * Hq] or nullptr
     int32_t out_dtype;
     int32_t splits_per_wg;      // MFMA kernel: consecutive splits per workgroup (2 or 4)
+    // one split per row (max_splits == 1): the partial kernel writes the
+    // result itself to out / lse (out_dtype) and no partials
+    int32_t direct;
     // whole-row fallback of unified max: the unified pass writes every row's
     // partial and only flags (row_fallback); a second, synchronized pass
     // (recompute_rows) rewrites every split of the rows flagged anywhere
     int32_t row_fallback;
     int32_t recompute_rows;
+    // A KV head's q_len * G query rows go in query tiles of tile_tokens whole
+    // query tokens (the last tile may be shorter); grid z = b * q_tiles + tile.
+    // (Last in the struct: the kernels' first parameter loads keep their shape.)
+    int32_t q_tiles;
+    int32_t tile_tokens;
+    int32_t i0;                 // device: first query token of the workgroup's tile
 };
 
 struct CombineParams {

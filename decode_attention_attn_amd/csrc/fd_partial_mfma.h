@@ -525,8 +525,9 @@ __device__ void scan_split(const PartialParams &p, int b, int kvh, int t0, int t
 }
 
 // Wave states of row tile rt (query rows 16 rt ..) -> the split's partial
-// for the rows in write_mask.
-template <int T, int D, int GMAX, int WAVES>
+// for the rows in write_mask (DIRECT: a row's only split, written as the
+// result to out and lse).
+template <int T, int D, int GMAX, int WAVES, bool DIRECT>
 __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<D, GMAX, WAVES> &sm, int b, int kvh,
                              int s, uint32_t write_mask, int rt, float vmul) {
     using C = MCfg<D, GMAX, WAVES>;
@@ -576,21 +577,31 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
             M = Mx;
         }
         if (g >= p.R || !((write_mask >> g) & 1u)) continue;
-        const size_t slot = row_slot(p, b, kvh, g, s);
         float inv = L > 0.f ? 1.f / L : 0.f;
         if constexpr (f8_of(T)) inv *= vmul;   // a stored V unit stands for the head's V scale
+        float a[C::SL];
 #pragma unroll
         for (int i = 0; i < C::SL; ++i) {
-            float a = st.o[i][r];
+            a[i] = st.o[i][r];
             if constexpr (WAVES == 2) {
                 const float xr = r == 0 ? x[i].x : r == 1 ? x[i].y : r == 2 ? x[i].z : x[i].w;
-                a = fmaf(xr, f1, a * f0);
+                a[i] = fmaf(xr, f1, a[i] * f0);
             }
-            p.part_o[slot * D + 16 * i + mrow] = a * inv;
         }
-        if (mrow == 0) {
-            p.part_m[slot] = (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY;
-            p.part_l[slot] = L;
+        const float m_nat = (L > 0.f && M != -INFINITY) ? M * kLn2 : -INFINITY;
+        if constexpr (DIRECT) {   // the row's only split: its partial is the result
+            const size_t row = query_row(p, b, kvh, g);
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) store_out(p.out, row * D + 16 * i + mrow, a[i] * inv, p.out_dtype);
+            if (mrow == 0 && p.lse) p.lse[row] = L > 0.f ? m_nat + logf(L) : -INFINITY;
+        } else {
+            const size_t slot = row_slot(p, b, kvh, g, s);
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) p.part_o[slot * D + 16 * i + mrow] = a[i] * inv;
+            if (mrow == 0) {
+                p.part_m[slot] = m_nat;
+                p.part_l[slot] = L;
+            }
         }
     }
 }
@@ -659,7 +670,7 @@ __device__ __forceinline__ void head_scales(const PartialParams &p, int kvh, flo
     }
 }
 
-template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI>
+template <int T, int D, int GMAX, int WAVES, bool PAGED, bool UNI, bool DIRECT>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(GMAX))))
 partial_mfma_kernel(const PartialParams pk) {
     using C = MCfg<D, GMAX, WAVES>;
@@ -678,10 +689,13 @@ partial_mfma_kernel(const PartialParams pk) {
     if (t0 >= t1) {
         if (threadIdx.x < R && !p.recompute_rows) {
             const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
-            p.part_m[slot] = -INFINITY;
-            p.part_l[slot] = 0.f;
+            if (!DIRECT) {
+                p.part_m[slot] = -INFINITY;
+                p.part_l[slot] = 0.f;
+            }
             if (p.flags) p.flags[slot] = 0;
         }
+        if (DIRECT && !p.recompute_rows) write_empty_rows<D>(p, b, kvh, 64 * WAVES);   // rows that see nothing
         return;
     }
     // whole-row fallback, second pass: only rows flagged in some split of the request
@@ -723,7 +737,7 @@ partial_mfma_kernel(const PartialParams pk) {
         const uint32_t keep = p.row_fallback ? all : all & ~badmask;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
-            finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, keep, rt, vmul);
+            finish_split<T, D, GMAX, WAVES, DIRECT>(p, st[rt], sm, b, kvh, s, keep, rt, vmul);
         if (badmask && !p.row_fallback) {   // synchronized recompute of the flagged heads
             if constexpr (WAVES > 1) __syncthreads();   // the hand-over area overlays the K tiles
 #pragma unroll
@@ -731,7 +745,7 @@ partial_mfma_kernel(const PartialParams pk) {
             scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm);
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
-                finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, badmask, rt, vmul);
+                finish_split<T, D, GMAX, WAVES, DIRECT>(p, st[rt], sm, b, kvh, s, badmask, rt, vmul);
         }
         if (threadIdx.x == 0 && badmask && p.fallback_count)
             atomicAdd(p.fallback_count, __builtin_popcount(badmask));
@@ -741,7 +755,7 @@ partial_mfma_kernel(const PartialParams pk) {
         scan_split<T, D, GMAX, WAVES, PAGED, false>(p, b, kvh, t0, t1, sc, lim, qop, st, sm);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
-            finish_split<T, D, GMAX, WAVES>(p, st[rt], sm, b, kvh, s, rows_to_write, rt, vmul);
+            finish_split<T, D, GMAX, WAVES, DIRECT>(p, st[rt], sm, b, kvh, s, rows_to_write, rt, vmul);
     }
     if (p.flags && threadIdx.x < R && !p.recompute_rows)
         p.flags[row_slot(p, b, kvh, threadIdx.x, s)] = (badmask >> threadIdx.x) & 1u;
@@ -939,21 +953,29 @@ inline int launch_waves(const PartialParams &p) {
     return (!f8_of(T) || p.R > 4) ? 1 : 2;
 }
 
-template <int T, int D, int GMAX, int WAVES, bool PAGED>
+template <int T, int D, int GMAX, int WAVES, bool PAGED, bool DIRECT = false>
 hipError_t launch_shaped(const PartialParams &p, hipStream_t stream) {
     dim3 grid(p.max_splits, p.Hkv, p.B * p.q_tiles);
-    if (p.unified)
-        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, true>), grid, dim3(64 * WAVES), 0, stream,
-                           p);
-    else
-        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, false>), grid, dim3(64 * WAVES), 0, stream,
-                           p);
+    if constexpr (DIRECT) {   // the synchronized softmax only (the host sends unified max to the merge path)
+        if (p.unified) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, false, true>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    } else if (p.unified) {
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, true, false>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    } else {
+        hipLaunchKernelGGL((partial_mfma_kernel<T, D, GMAX, WAVES, PAGED, false, false>), grid, dim3(64 * WAVES), 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 
 template <int T, int D, int GMAX, bool PAGED>
 hipError_t launch(const PartialParams &p, hipStream_t stream) {
     if (p.tickets) return launch_fused<T, D, GMAX, PAGED>(p, stream);
+    // one split per row, written as the result: one-wave workgroups (a
+    // separate instantiation keeps the other kernels free of its epilogue)
+    if (p.direct) return launch_shaped<T, D, GMAX, 1, PAGED, true>(p, stream);
     if constexpr (GMAX > 4 || !f8_of(T)) {
         if (launch_waves<T>(p) == 1) return launch_shaped<T, D, GMAX, 1, PAGED>(p, stream);
     }

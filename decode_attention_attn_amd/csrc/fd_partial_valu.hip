@@ -214,12 +214,19 @@ __device__ void finish_split(const PartialParams &p, State<DT, D, GMAX> &st, Sme
             L += sm.l[w][g] * f;
             A += sm.acc[w][g][dim] * f;
         }
-        const size_t slot = row_slot(p, b, kvh, g, s);
         float o = L > 0.f ? A / L : 0.f;
         if constexpr (DT == FP8) o *= vmul;
+        const float m_nat = (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY;
+        if (!FUSED && p.direct) {   // the row's only split: its partial is the result
+            const size_t row = query_row(p, b, kvh, g);
+            store_out(p.out, row * D + dim, o, p.out_dtype);
+            if (dim == 0 && p.lse) p.lse[row] = L > 0.f ? m_nat + logf(L) : -INFINITY;
+            continue;
+        }
+        const size_t slot = row_slot(p, b, kvh, g, s);
         store_partial<FUSED>(&p.part_o[slot * D + dim], o);
         if (dim == 0) {
-            store_partial<FUSED>(&p.part_m[slot], (L > 0.f && mm != -INFINITY) ? mm * kLn2 : -INFINITY);
+            store_partial<FUSED>(&p.part_m[slot], m_nat);
             store_partial<FUSED>(&p.part_l[slot], L);
         }
     }
@@ -254,13 +261,13 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     if (t0 >= t1) {   // empty split: nothing to read
         if (threadIdx.x < G && !p.recompute_rows) {
             const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
-            if (!FUSED) {
+            if (!FUSED && !p.direct) {
                 p.part_m[slot] = -INFINITY;
                 p.part_l[slot] = 0.f;
             }
             if (p.flags) p.flags[slot] = 0;
         }
-        if (FUSED && tl <= 0 && s == 0) write_empty_rows<D>(p, b, kvh, kThreads);
+        if ((FUSED || p.direct) && !p.recompute_rows && tl <= 0 && s == 0) write_empty_rows<D>(p, b, kvh, kThreads);
         return;
     }
     // whole-row fallback, second pass: only rows flagged in some split of the request

@@ -134,9 +134,14 @@ typedef enum fd_kernel {
  *   Softmax with Unified Max Value", its design choices: a reduction across
  *   workers by atomics instead of a relaunch).  Needs the workspace's ticket
  *   area to be zero when the call starts (see fd_workspace_bytes); requires
- *   B * Hkv <= 65536 and reports shapes whose merge does not fit one
- *   workgroup, and FD_FALLBACK_ROW, FD_ERR_UNSUPPORTED.
- * AUTO: whichever the library measured faster for the shape.
+ *   B * (query tiles) * Hkv <= 65536 and reports shapes whose merge does not
+ *   fit one workgroup, and FD_FALLBACK_ROW, FD_ERR_UNSUPPORTED.
+ * AUTO: whichever the library measured faster for the shape; with
+ *   max_splits == 1 in FD_SOFTMAX_SYNC mode neither: each row's one split is
+ *   its result, which the partial kernel writes to out and lse itself (the
+ *   workspace's partials are then left unwritten), as the Flash-Decoding
+ *   page's "Production Implementation Guidelines" drop the split once batch
+ *   and heads fill the GPU.
  * Both give the same result to within floating-point rounding (the merge is
  * exact; FUSED takes it as a tree: the splits of a workgroup, then the
  * workgroups).  fd_decode_attn_partial and fd_decode_attn_combine ignore it. */

@@ -199,6 +199,10 @@ WORKLOADS = {
     # no split size is given for this shape: 1024 is what the library's split heuristic picks for it
     "umax_stress": Workload("umax_stress", B=4, Hq=64, Hkv=8, d=128, dtype="bf16", split=1024, N=131072,
                             stress_frac=0.02, stress_scale=8.0),
+    # a whole 4k prompt as queries (prefill): every token attends causally to
+    # the tokens up to it; one split per query tile (the tiles alone fill the GPU)
+    "prefill_gqa_4k": Workload("prefill_gqa_4k", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=4096, N=4096,
+                               q_len=4096),
     # the long-context GQA shape with an 8-bit cache (scale 1/64: N(0, 1) draws stored as 64 x)
     "long_gqa_32k_fp8": Workload("long_gqa_32k_fp8", B=1, Hq=32, Hkv=8, d=128, dtype="fp8", split=256,
                                  N=32768, k_scale=1.0 / 64, v_scale=1.0 / 64),

@@ -45,6 +45,24 @@ def test_algorithmic_bytes_count_the_block_table_entries_read():
     assert a["units"] == (17 + 16 + 1000) * 2
 
 
+def test_flops_and_bound_decode_and_prefill():
+    # decode: 4 d flops per (query row, token): 32 heads x 32768 tokens; HBM-bound
+    inp = synth.make_inputs(synth.WORKLOADS["long_gqa_32k"], poison_tail=False)
+    a = bench.algorithmic_bytes(inp)
+    assert a["flops"] == 4 * 128 * 32 * 32768
+    assert bench.roofline_bound(inp.w, "auto", a) == ("hbm", bench.HBM_PEAK_GBPS)
+    # a whole 4k prompt: token i sees i + 1 tokens, sum N (N + 1) / 2; matrix-bound
+    w = synth.WORKLOADS["prefill_gqa_4k"]
+    inp = synth.make_inputs(w, poison_tail=False)
+    a = bench.algorithmic_bytes(inp)
+    assert a["flops"] == 4 * 128 * 32 * (4096 * 4097 // 2)
+    assert bench.roofline_bound(w, "auto", a) == ("mfma", bench.MFMA_PEAK_TFLOPS)
+    # chunk of the last 3 of 5 tokens and a request shorter than its queries
+    w = synth.with_lens(synth.Workload("c", B=2, Hq=2, Hkv=1, d=8, dtype="f32", split=8, N=1, q_len=3), (5, 2))
+    a = bench.algorithmic_bytes(synth.make_inputs(w, poison_tail=False))
+    assert a["flops"] == 4 * 8 * 2 * ((3 + 4 + 5) + (0 + 1 + 2))
+
+
 def _write_counters(d: Path, counter, rows):
     d.mkdir(parents=True)
     with open(d / "x_counter_collection.csv", "w", newline="") as f:

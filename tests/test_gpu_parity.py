@@ -811,6 +811,71 @@ def test_query_tiles_match_untiled_rows_bitwise():
             assert np.array_equal(res["lse"][r], r1["lse"][r_1]), (part, b)
 
 
+# ----------------------------------------------------------------------------
+# one split per row (max_splits == 1): under AUTO the partial kernel writes
+# out and lse itself, with no partials and no merge
+# ----------------------------------------------------------------------------
+DIRECT_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d)
+    ("mfma", "bf16", 32, 8, 1, 128), ("mfma", "f16", 8, 8, 1, 64), ("mfma", "fp8", 32, 8, 1, 128),
+    ("mfma", "bf16", 32, 8, 20, 128), ("valu", "f32", 16, 8, 1, 128), ("valu", "bf16", 8, 8, 40, 64),
+]
+
+
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", DIRECT_CASES)
+def test_direct_single_split(kernel, dtype, Hq, Hkv, q_len, d, page):
+    extra = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if dtype == "fp8" else {}
+    base = synth.Workload("direct", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=1024, N=1, page_size=page,
+                          q_len=q_len, **extra)
+    # an empty request, one shorter than its query tokens, one at the split's size
+    inp = synth.make_inputs(synth.with_lens(base, (700, 0, 3, 1024, 129)))
+    run = Run(inp)
+    res = _skip_unsupported(lambda: run.run(kernel=kernel, full=True))
+    assert res["desc"].max_splits == 1
+    what = f"direct {kernel} {dtype} q_len={q_len} d={d} page={page}"
+    ft.check_exact(res, inp, what=what)
+    r0 = q_len * Hq                                  # the empty request's rows
+    assert np.all(res["out"][r0:2 * r0] == 0.0) and np.all(res["lse"][r0:2 * r0] == -np.inf)
+    sep = run.run(kernel=kernel, full=True, merge="separate")
+    # (the direct launch takes one-wave workgroups, the separate one may take
+    # two, which round the split's sums in another order)
+    ft.assert_close(res["out"], sep["out"], dtype, f"{what} vs separate")
+    ft.assert_close(res["lse"], sep["lse"], dtype, f"{what} lse vs separate")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("fallback", ["split", "row"])
+def test_single_split_unified_max(kernel, fallback):
+    """One split per row under unified max: AUTO keeps the partials and the
+    merge there (the direct output is the synchronized softmax's)."""
+    base = synth.Workload("directu", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=2048, N=1, q_len=2,
+                          stress_frac=0.02, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, (2000, 700, 1)))
+    phi, lo, hi = -12.0, -12.0, 12.0
+    res = _skip_unsupported(lambda: Run(inp).run(kernel=kernel, full=True, mode="unified", phi=phi, lo=lo, hi=hi,
+                                                 fallback=fallback))
+    must, may = ft.flag_bounds(inp, 2048, 1, phi, lo, hi)
+    got = res["flags"].astype(bool)
+    assert np.all(got[must]) and not np.any(got[~may]) and got.any()
+    ft.check_exact(res, inp, what=f"single split unified {kernel} {fallback}")
+
+
+def test_prefill_gqa_4k_full():
+    """A whole 4k prompt as queries (32 heads on 8 KV heads, one split): every
+    row against the oracle, through the AUTO entry point (direct output) and
+    the partial + combine kernels."""
+    w = synth.WORKLOADS["prefill_gqa_4k"]
+    say(f"[{w.name}] generating")
+    inp = synth.make_inputs(w)
+    run = Run(inp)
+    res = run.run(full=True)
+    e1, e2 = ft.check_exact(res, inp, what=w.name)
+    say(f"[{w.name}] direct max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+    res = run.run()
+    ft.check_exact(res, inp, what=f"{w.name} partial + combine")
+    ft.check_partials(res, inp, w.split, what=w.name)
+
+
 @pytest.mark.parametrize("q_len,Hq", [(4, 16), (4, 64)])
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_multi_query_unified_max(kernel, q_len, Hq):
