@@ -351,18 +351,16 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A block's K and V registers -> the wave's LDS tiles (the registers are
-// free again afterwards).
-template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], const uint4 (&vr)[KLoad<T, D>::LI],
-                                            MSmem<D, GMAX, WAVES> &sm) {
-    using C = MCfg<D, GMAX, WAVES>;
+// A block's K and V registers -> LDS tiles (the registers are free again
+// afterwards).
+template <int T, int D, bool UNIFIED>
+__device__ __forceinline__ void write_tiles_at(const uint4 (&kr)[KLoad<T, D>::LI],
+                                               const uint4 (&vr)[KLoad<T, D>::LI], char *ktile, char *vtile) {
+    using C = MCfg<D, 1, 1>;
     using L = KLoad<T, D>;
     constexpr int DT = op_of(T);
-    const int lane = threadIdx.x & 63, wave = head_wave<WAVES>();
+    const int lane = threadIdx.x & 63;
     const int rg = lane / L::LPR, ch = lane % L::LPR;
-    char *ktile = reinterpret_cast<char *>(sm.k[wave]);
-    char *vtile = reinterpret_cast<char *>(sm.v[wave]);
     // tiles: 16-byte chunk c of row r lives at slot chunk_slot(c) ^ (r & (LPR-1))
     // (K) and chunk_slot(c) ^ (2 * (r & (LPR/2 - 1))) (V), LPR = D / 8 chunks per row
 #pragma unroll
@@ -385,20 +383,27 @@ __device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], 
     }
 }
 
+// ... into the wave's private tiles.
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void write_tiles(const uint4 (&kr)[KLoad<T, D>::LI], const uint4 (&vr)[KLoad<T, D>::LI],
+                                            MSmem<D, GMAX, WAVES> &sm) {
+    const int wave = head_wave<WAVES>();
+    write_tiles_at<T, D, UNIFIED>(kr, vr, reinterpret_cast<char *>(sm.k[wave]), reinterpret_cast<char *>(sm.v[wave]));
+}
+
 // One block from the wave's tiles into the running state.
 // lim: this lane's query row (lane % 16) sees tokens < lim of the split;
 // sc: the score scale in log2 units (scale * log2(e), times the KV head's K
 // scale for 8-bit caches)
-template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
-__device__ __forceinline__ void compute_tiles(const PartialParams &p, const BlockRows &br, int lim, float sc,
-                                              const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
-                                              MSmem<D, GMAX, WAVES> &sm) {
-    using C = MCfg<D, GMAX, WAVES>;
+// ktile, vtile: the block's LDS tiles; corr: the wave's 16 rescale slots.
+template <int T, int D, int GMAX, bool UNIFIED>
+__device__ __forceinline__ void compute_tiles_at(const PartialParams &p, const BlockRows &br, int lim, float sc,
+                                                 const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
+                                                 const char *ktile, const char *vtile, float *corr_lds) {
+    using C = MCfg<D, GMAX, 1>;
     constexpr int DT = op_of(T);
-    const int lane = threadIdx.x & 63, wave = head_wave<WAVES>();
+    const int lane = threadIdx.x & 63;
     const int mrow = lane & 15, mq = lane >> 4;                 // MFMA coordinates
-    const char *ktile = reinterpret_cast<const char *>(sm.k[wave]);
-    const char *vtile = reinterpret_cast<const char *>(sm.v[wave]);
 
     // ---- S^T = K q^T on the matrix cores
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -440,9 +445,9 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
         }
         // rescale the P x V accumulators (heads on rows 4 * (l / 16) + r)
         if (__any(moved)) {
-            if (lane < 16) sm.corr[wave][lane] = corr;
+            if (lane < 16) corr_lds[lane] = corr;
             wave_lds_sync();
-            const float4 cf = *reinterpret_cast<const float4 *>(&sm.corr[wave][4 * mq]);
+            const float4 cf = *reinterpret_cast<const float4 *>(&corr_lds[4 * mq]);
 #pragma unroll
             for (int i = 0; i < C::SL; ++i) {
                 st.o[i][0] *= cf.x;
@@ -486,6 +491,16 @@ __device__ __forceinline__ void compute_tiles(const PartialParams &p, const Bloc
         st.o[i] = mfma16x16x16<PT>(phi, b, st.o[i]);
         if constexpr (!pv_single(T, UNIFIED)) st.o[i] = mfma16x16x16<PT>(plo, b, st.o[i]);
     }
+}
+
+// ... from the wave's private tiles.
+template <int T, int D, int GMAX, int WAVES, bool UNIFIED>
+__device__ __forceinline__ void compute_tiles(const PartialParams &p, const BlockRows &br, int lim, float sc,
+                                              const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
+                                              MSmem<D, GMAX, WAVES> &sm) {
+    const int wave = head_wave<WAVES>();
+    compute_tiles_at<T, D, GMAX, UNIFIED>(p, br, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[wave]),
+                                          reinterpret_cast<const char *>(sm.v[wave]), sm.corr[wave]);
 }
 
 // One wave's share of the split: blocks wave, wave + WAVES, ...  Paged caches
@@ -762,6 +777,135 @@ partial_mfma_kernel(const PartialParams pk) {
 }
 
 // ---------------------------------------------------------------------------
+// query tiles sharing K and V (a prompt's worth of query rows per KV head)
+// ---------------------------------------------------------------------------
+// Four waves, one query tile each (up to 32 rows, two 16-row matrix tiles),
+// scan the same tokens of a split: of every 64 tokens each wave loads one
+// 16-token block, the four blocks pass through LDS once, and every wave runs
+// its rows against all four.  Per query row, K and V come through the cache
+// hierarchy a quarter as often as with one workgroup per tile (the handbook
+// page's forward kernel likewise stages K and V tiles in shared memory for a
+// block of query rows, section "A working FlashAttention forward kernel").
+// Synchronized softmax; each wave writes its rows' partials (or, DIRECT, the
+// result) like a one-wave workgroup.
+constexpr int kShareWaves = 4;
+
+template <int D>
+struct PSmem {
+    uint4 k[kShareWaves][kBlk * D * 2 / 16];     // block j of the 64 tokens, loaded by wave j
+    uint4 v[kShareWaves][kBlk * D * 2 / 16];
+    float corr[kShareWaves][16];                 // each wave's rescale slots
+};
+
+// Register budget: two waves per SIMD (two workgroups per CU).
+template <int T, int D, bool PAGED, bool DIRECT>
+__global__ void __launch_bounds__(64 * kShareWaves) __attribute__((amdgpu_waves_per_eu(2)))
+shared_kv_mfma_kernel(const PartialParams pk) {
+    constexpr int GMAX = 32, NT = row_tiles(GMAX), W = kShareWaves;
+    using C = MCfg<D, GMAX, 1>;
+    using L = KLoad<T, D>;
+    static_assert(sizeof(PSmem<D>) <= 65536, "LDS budget of one workgroup");
+    __shared__ PSmem<D> sm;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // grid z = b * groups + j: request b, tile group groups - 1 - j (the
+    // groups of later query tokens see more of the cache and start first)
+    const int groups = (pk.q_tiles + W - 1) / W;
+    const int b = (int)blockIdx.z / groups;
+    const int grp = groups - 1 - ((int)blockIdx.z - b * groups);
+    const int kvh = blockIdx.y;
+    const int s = split_index(blockIdx.x, blockIdx.z, kvh, pk.Hkv, pk.max_splits);
+    const int tile = grp * W + w, last = min(grp * W + W - 1, pk.q_tiles - 1);
+    PartialParams p = pk;                        // this wave's tile
+    p.i0 = tile * pk.tile_tokens;
+    p.R = tile < pk.q_tiles ? min(pk.tile_tokens, pk.q_len - p.i0) * pk.G : 0;
+    PartialParams pl = pk;                       // the group's last tile: its tokens bound the scan
+    pl.i0 = last * pk.tile_tokens;
+    pl.R = min(pk.tile_tokens, pk.q_len - pl.i0) * pk.G;
+    const int R = p.R;
+    const int len = request_len(pk.seq_lens, b, pk.kv_capacity, pk.max_splits * pk.split);
+    const int t0 = s * pk.split;
+    const int t1 = min(t0 + pk.split, tile_len(pl, len));
+
+    if (t0 >= t1) {   // no row of the group sees a token of this split
+        if (DIRECT) {
+            for (int idx = lane; idx < R * D; idx += 64)
+                store_out(p.out, query_row(p, b, kvh, idx / D) * D + idx % D, 0.f, p.out_dtype);
+            if (lane < R && p.lse) p.lse[query_row(p, b, kvh, lane)] = -INFINITY;
+        } else if (lane < R) {
+            const size_t slot = row_slot(p, b, kvh, lane, s);
+            p.part_m[slot] = -INFINITY;
+            p.part_l[slot] = 0.f;
+        }
+        if (p.flags && lane < R) p.flags[row_slot(p, b, kvh, lane, s)] = 0;
+        return;
+    }
+
+    float sc, vmul;
+    head_scales<T>(p, kvh, sc, vmul);
+    uint4 qop[NT][C::KS];
+    int lim[NT];
+    load_q_operand<D, GMAX>(p, b, kvh, len, t1, qop, lim);
+    MState<D, GMAX> st[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) st[rt].init(-INFINITY);
+    const int wlen = R > 0 ? min(tile_len(p, len), t1) : t0;   // this wave's rows see tokens < wlen
+
+    const auto off = lane_offsets<T, D>(p);
+    const PageCache pc = load_pages<PAGED>(p, b, t0, t1);
+    const int nsup = (t1 - t0 + W * kBlk - 1) / (W * kBlk);
+    // one register set, as in the one-wave kernel: the next 64 tokens' loads
+    // are in flight during the matrix work on these
+    BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + w * kBlk, t1);
+    uint4 kr[L::LI], vr[L::LI];
+    load_block<T, D>(p, br, t1, off, kr, vr);
+    for (int k = 0; k < nsup; ++k) {
+        const int tsup = t0 + k * W * kBlk;
+        write_tiles_at<T, D, false>(kr, vr, reinterpret_cast<char *>(sm.k[w]), reinterpret_cast<char *>(sm.v[w]));
+        __syncthreads();                          // all four blocks in LDS
+        const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tsup + W * kBlk + w * kBlk, t1);
+        load_block<T, D>(p, bn, t1, off, kr, vr);
+        for (int j = 0; j < W; ++j) {
+            const int tb = tsup + j * kBlk;
+            if (tb >= wlen) break;                // the rest lie past this wave's rows
+            const BlockRows bj = block_rows<D, PAGED>(p, pc, b, kvh, tb, t1);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                compute_tiles_at<T, D, GMAX, false>(p, bj, lim[rt], sc, qop[rt], st[rt],
+                                                    reinterpret_cast<const char *>(sm.k[j]),
+                                                    reinterpret_cast<const char *>(sm.v[j]), sm.corr[w]);
+        }
+        __syncthreads();                          // every wave's reads before the next writes
+    }
+    if (R > 0) {
+        const uint32_t all = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
+        auto &one = *reinterpret_cast<MSmem<D, GMAX, 1> *>(&sm);   // unused by a one-wave epilogue
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) finish_split<T, D, GMAX, 1, DIRECT>(p, st[rt], one, b, kvh, s, all, rt, vmul);
+        if (p.flags && lane < R) p.flags[row_slot(p, b, kvh, lane, s)] = 0;
+    }
+}
+
+template <int T, int D, bool PAGED>
+hipError_t launch_shared_kv(const PartialParams &p, hipStream_t stream) {
+    const int groups = (p.q_tiles + kShareWaves - 1) / kShareWaves;
+    dim3 grid(p.max_splits, p.Hkv, p.B * groups);
+    if (p.direct)
+        hipLaunchKernelGGL((shared_kv_mfma_kernel<T, D, PAGED, true>), grid, dim3(64 * kShareWaves), 0, stream, p);
+    else
+        hipLaunchKernelGGL((shared_kv_mfma_kernel<T, D, PAGED, false>), grid, dim3(64 * kShareWaves), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Whether a launch takes the shared-K/V kernel: four or more query tiles per
+// KV head (a prompt's worth of rows; fewer leave waves idle), synchronized
+// softmax, partials or the direct result (the single-launch merge and the
+// unified-max passes keep one tile per workgroup).
+inline bool use_shared_kv(const PartialParams &p) {
+    return p.q_tiles >= kShareWaves && !p.unified && !p.tickets && !p.recompute_rows && !p.row_fallback;
+}
+
+// ---------------------------------------------------------------------------
 // single launch: partials and their merge in one kernel
 // ---------------------------------------------------------------------------
 // A workgroup covers SW consecutive splits of one (request, KV head), one
@@ -989,6 +1133,8 @@ hipError_t by_paged(const PartialParams &p, hipStream_t s) {
 
 template <int T, int D>
 hipError_t by_group(const PartialParams &p, hipStream_t s) {
+    if (use_shared_kv(p))   // tiles of more than 16 rows (the host balances them): GMAX 32
+        return p.page_size ? launch_shared_kv<T, D, true>(p, s) : launch_shared_kv<T, D, false>(p, s);
     if (p.R <= 1) return by_paged<T, D, 1>(p, s);
     if (p.R <= 2) return by_paged<T, D, 2>(p, s);
     if (p.R <= 4) return by_paged<T, D, 4>(p, s);

@@ -736,6 +736,10 @@ QT_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d): tiles of the kernel's rows
     ("valu", "bf16", 8, 8, 40, 64),       # G=1: tiles of 14, 14, 12
     ("valu", "fp8", 32, 8, 6, 128),       # G=4: 2 tiles of 3
     ("auto", "f32", 64, 8, 4, 128),       # G=8, 32 rows: 2 VALU tiles of 2 tokens
+    # four or more tiles: workgroups of four tiles sharing each K/V block
+    ("mfma", "fp8", 32, 8, 40, 128),      # G=4: 5 tiles of 8 (a second group with one tile)
+    ("mfma", "bf16", 64, 8, 33, 128),     # G=8: 9 tiles (4 tokens, the last 1)
+    ("mfma", "f16", 16, 16, 150, 64),     # G=1: 5 tiles of 30
 ]
 
 
@@ -818,6 +822,7 @@ def test_query_tiles_match_untiled_rows_bitwise():
 DIRECT_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d)
     ("mfma", "bf16", 32, 8, 1, 128), ("mfma", "f16", 8, 8, 1, 64), ("mfma", "fp8", 32, 8, 1, 128),
     ("mfma", "bf16", 32, 8, 20, 128), ("valu", "f32", 16, 8, 1, 128), ("valu", "bf16", 8, 8, 40, 64),
+    ("mfma", "bf16", 32, 8, 40, 128), ("mfma", "fp8", 16, 16, 130, 64),   # shared-K/V tile groups
 ]
 
 
