@@ -42,6 +42,8 @@ MUTATIONS = [
     ("whole-row fallback only recomputes the flagged split", "if (whole_row ? row_bad : bad) {", "if (bad) {"),
     ("per-head K scale by query head", "double ks = k_scale_of(p, kvh);", "double ks = k_scale_of(p, h % p->Hkv);"),
     ("per-head V scale of head 0", "double vs = v_scale_of(p, kvh);", "double vs = v_scale_of(p, 0);"),
+    ("causal limit one short", "int lim = n - p->q_len + i + 1;", "int lim = n - p->q_len + i;"),
+    ("causal window from the first token", "int lim = n - p->q_len + i + 1;", "int lim = i + 1;"),
 ]
 
 
