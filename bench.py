@@ -365,7 +365,7 @@ def kernel_key(name):
     split-partial kernel, the combine, or the name itself."""
     if "fused_mfma_kernel" in name:
         return "fused"
-    if "partial" in name:
+    if "partial" in name or "shared_kv" in name:
         return PARTIAL_KERNEL
     if "combine" in name:
         return "combine"
@@ -425,8 +425,13 @@ def main():
                     help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE runs into profiles/<workload>_pmc.json")
     args = ap.parse_args()
     if args.merge is None:
+        # contiguous caches: partial and combine timed apart (the roofline is the
+        # partial kernel's), except with one split per row, where the library
+        # writes the result from the partial kernel (AUTO) and has no combine
         import synth
-        args.merge = "auto" if synth.WORKLOADS[args.workload].page_size else "separate"
+        w0 = synth.WORKLOADS[args.workload]
+        one_split = -(-w0.N // (args.split or w0.split)) == 1
+        args.merge = "auto" if (w0.page_size or one_split) else "separate"
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
@@ -462,8 +467,8 @@ def main():
         keys = ["fused"]
     elif args.merge == "separate":
         keys = [PARTIAL_KERNEL, "combine"]
-    else:   # auto: whichever the library took
-        keys = [["fused"], [PARTIAL_KERNEL, "combine"]]
+    else:   # auto: whichever the library took (the partial kernel alone: one split, direct output)
+        keys = [["fused"], [PARTIAL_KERNEL, "combine"], [PARTIAL_KERNEL]]
     traffic = traffic_from_profile(w.name, keys, run_settings(args))
     bound, peak = roofline_bound(w, args.kernel, alg)
     if bound == "hbm":

@@ -108,3 +108,5 @@ def test_kernel_keys():
                             "(fd::PartialParams)") == bench.PARTIAL_KERNEL
     assert bench.kernel_key("void fd::(anonymous namespace)::combine_kernel<128, 128, 256, true>"
                             "(fd::CombineParams)") == "combine"
+    assert bench.kernel_key("void fd::(anonymous namespace)::shared_kv_mfma_kernel<2, 128, false, true>"
+                            "(fd::PartialParams)") == bench.PARTIAL_KERNEL
