@@ -136,13 +136,17 @@ constexpr int kF8 = 16;
 __host__ __device__ constexpr int op_of(int T) { return T & 15; }
 __host__ __device__ constexpr bool f8_of(int T) { return T >= kF8; }
 
-// P x V operand type.  8-bit caches with the synchronized softmax take f16
-// for both operands: the widened V values are exact in f16 and every
-// probability lies in [0, 1], so one MFMA on P rounded to nearest f16
-// (relative error <= 2^-11, absolute <= 2^-25 below the normal range)
-// replaces the high/residual pair.  The unified-max softmax keeps the pair in
-// the cache's operand type, since e^{s - phi} may exceed f16's range.
-__host__ __device__ constexpr bool pv_single(int T, bool UNIFIED) { return f8_of(T) && !UNIFIED; }
+// P x V operand type.  f16 caches, and 8-bit caches (whose widened V values
+// are exact in f16), take f16 for both operands under the synchronized
+// softmax: every probability lies in [0, 1], so one MFMA on P rounded to
+// nearest f16 (relative error <= 2^-11, absolute <= 2^-25 below the normal
+// range) replaces the high/residual pair (Llama-2-shaped MHA, f16: partial
+// 13.40-13.44 against 13.57-13.63 us).  bf16 caches keep the pair, bf16's
+// 8-bit significand being too coarse for P alone, and so does the
+// unified-max softmax, since e^{s - phi} may exceed f16's range.
+__host__ __device__ constexpr bool pv_single(int T, bool UNIFIED) {
+    return (f8_of(T) || op_of(T) == F16) && !UNIFIED;
+}
 __host__ __device__ constexpr int pv_type(int T, bool UNIFIED) { return pv_single(T, UNIFIED) ? F16 : op_of(T); }
 
 // How a block's cache rows are loaded: 16 bytes per lane, LPR lanes per row.
