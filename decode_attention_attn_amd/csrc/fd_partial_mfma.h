@@ -498,64 +498,93 @@ __device__ __forceinline__ void compute_tiles_at(const PartialParams &p, const B
 }
 
 // Two consecutive blocks (32 tokens) from their LDS tiles into the running
-// state, synchronized softmax: the scores of both, one running-max update for
-// the 32, and O += P V on 16x16x32 instructions, whose 32-long k dimension
-// takes this lane's four tokens of the first block (k = 8 (lane / 16) + 0..3)
-// and its four of the second (+ 4..7) in P and in V alike.  Half the P x V
-// instructions of two single-block steps, each doing twice the work.
+// states of all of the wave's 16-row tiles, synchronized softmax: the scores
+// of both blocks, one running-max update for the 32, and O += P V on
+// 16x16x32 instructions, whose 32-long k dimension takes this lane's four
+// tokens of the first block (k = 8 (lane / 16) + 0..3) and its four of the
+// second (+ 4..7) in P and in V alike.  Half the P x V instructions of two
+// single-block steps, each doing twice the work; every K and V operand is
+// read from LDS once for all row tiles.  corr_lds: 16 slots per row tile.
 template <int T, int D, int GMAX>
 __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const BlockRows &ba, const BlockRows &bb,
-                                                int lim, float sc, const uint4 (&qop)[D / 32], MState<D, GMAX> &st,
-                                                const char *ka, const char *va, const char *kb, const char *vb,
-                                                float *corr_lds) {
+                                                const int (&lim)[row_tiles(GMAX)], float sc,
+                                                const uint4 (&qop)[row_tiles(GMAX)][D / 32],
+                                                MState<D, GMAX> (&st)[row_tiles(GMAX)], const char *ka,
+                                                const char *va, const char *kb, const char *vb, float *corr_lds) {
     using C = MCfg<D, GMAX, 1>;
-    constexpr int DT = op_of(T);
+    constexpr int DT = op_of(T), NT = row_tiles(GMAX);
     const int lane = threadIdx.x & 63;
     const int mrow = lane & 15, mq = lane >> 4;
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
         const int slot = chunk_slot<T>(4 * ks + mq) ^ (mrow & (C::LPR - 1));
         const uint4 a0 = *reinterpret_cast<const uint4 *>(ka + mrow * C::ROWB + slot * 16);
         const uint4 a1 = *reinterpret_cast<const uint4 *>(kb + mrow * C::ROWB + slot * 16);
-        acc[0] = mfma16x16x32<DT>(a0, qop[ks], acc[0]);
-        acc[1] = mfma16x16x32<DT>(a1, qop[ks], acc[1]);
-    }
-    float s[2][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        s[0][r] = ba.page_ok && ba.tb + 4 * mq + r < lim ? acc[0][r] * sc : -INFINITY;
-        s[1][r] = bb.page_ok && bb.tb + 4 * mq + r < lim ? acc[1][r] * sc : -INFINITY;
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(st.m, mt);
-    const float corr = rescale(st.m, mn);
-    const bool moved = mn != st.m;
-    st.m = mn;
-    st.l *= corr;
-    float pr[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pr[h][r] = mn == -INFINITY ? 0.f : exp2_fast(s[h][r] - mn);
-            st.l += pr[h][r];
+        for (int rt = 0; rt < NT; ++rt) {
+            acc[rt][0] = mfma16x16x32<DT>(a0, qop[rt][ks], acc[rt][0]);
+            acc[rt][1] = mfma16x16x32<DT>(a1, qop[rt][ks], acc[rt][1]);
         }
     }
-    if (__any(moved)) {
-        if (lane < 16) corr_lds[lane] = corr;
-        wave_lds_sync();
-        const float4 cf = *reinterpret_cast<const float4 *>(&corr_lds[4 * mq]);
+    auto pack8 = [](const s16x4 &x, const s16x4 &y) {
+        const uint2 u = __builtin_bit_cast(uint2, x), w = __builtin_bit_cast(uint2, y);
+        return make_uint4(u.x, u.y, w.x, w.y);
+    };
+    uint4 phi[NT], plo[NT];
 #pragma unroll
-        for (int i = 0; i < C::SL; ++i) {
-            st.o[i][0] *= cf.x;
-            st.o[i][1] *= cf.y;
-            st.o[i][2] *= cf.z;
-            st.o[i][3] *= cf.w;
+    for (int rt = 0; rt < NT; ++rt) {
+        float s[2][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[0][r] = ba.page_ok && ba.tb + 4 * mq + r < lim[rt] ? acc[rt][0][r] * sc : -INFINITY;
+            s[1][r] = bb.page_ok && bb.tb + 4 * mq + r < lim[rt] ? acc[rt][1][r] * sc : -INFINITY;
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        MState<D, GMAX> &t = st[rt];
+        const float mn = fmaxf(t.m, mt);
+        const float corr = rescale(t.m, mn);
+        const bool moved = mn != t.m;
+        t.m = mn;
+        t.l *= corr;
+        float pr[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[h][r] = mn == -INFINITY ? 0.f : exp2_fast(s[h][r] - mn);
+                t.l += pr[h][r];
+            }
+        }
+        if (__any(moved)) {
+            float *cs = corr_lds + 16 * rt;
+            if (lane < 16) cs[lane] = corr;
+            wave_lds_sync();
+            const float4 cf = *reinterpret_cast<const float4 *>(&cs[4 * mq]);
+#pragma unroll
+            for (int i = 0; i < C::SL; ++i) {
+                t.o[i][0] *= cf.x;
+                t.o[i][1] *= cf.y;
+                t.o[i][2] *= cf.z;
+                t.o[i][3] *= cf.w;
+            }
+        }
+        if constexpr (pv_single(T, false)) {
+            const f16x4 h0 = {(_Float16)pr[0][0], (_Float16)pr[0][1], (_Float16)pr[0][2], (_Float16)pr[0][3]};
+            const f16x4 h1 = {(_Float16)pr[1][0], (_Float16)pr[1][1], (_Float16)pr[1][2], (_Float16)pr[1][3]};
+            phi[rt] = pack8(__builtin_bit_cast(s16x4, h0), __builtin_bit_cast(s16x4, h1));
+        } else {
+            s16x4 h0, l0, h1, l1;
+            split_probs<DT>(pr[0], h0, l0);
+            split_probs<DT>(pr[1], h1, l1);
+            phi[rt] = pack8(h0, h1);
+            plo[rt] = pack8(l0, l1);
         }
     }
     constexpr int PT = pv_type(T, false);
@@ -567,27 +596,14 @@ __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const Bl
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4 *)(vtile + vrow * C::ROWB + slot * 16 + (dim & 7) * 2));
     };
-    auto pack8 = [](const s16x4 &x, const s16x4 &y) {
-        const uint2 u = __builtin_bit_cast(uint2, x), w = __builtin_bit_cast(uint2, y);
-        return make_uint4(u.x, u.y, w.x, w.y);
-    };
-    uint4 phi, plo;
-    if constexpr (pv_single(T, false)) {
-        const f16x4 h0 = {(_Float16)pr[0][0], (_Float16)pr[0][1], (_Float16)pr[0][2], (_Float16)pr[0][3]};
-        const f16x4 h1 = {(_Float16)pr[1][0], (_Float16)pr[1][1], (_Float16)pr[1][2], (_Float16)pr[1][3]};
-        phi = pack8(__builtin_bit_cast(s16x4, h0), __builtin_bit_cast(s16x4, h1));
-    } else {
-        s16x4 h0, l0, h1, l1;
-        split_probs<DT>(pr[0], h0, l0);
-        split_probs<DT>(pr[1], h1, l1);
-        phi = pack8(h0, h1);
-        plo = pack8(l0, l1);
-    }
 #pragma unroll
     for (int i = 0; i < C::SL; ++i) {
         const uint4 b = pack8(read_v(va, i), read_v(vb, i));
-        st.o[i] = mfma16x16x32<PT>(phi, b, st.o[i]);
-        if constexpr (!pv_single(T, false)) st.o[i] = mfma16x16x32<PT>(plo, b, st.o[i]);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            st[rt].o[i] = mfma16x16x32<PT>(phi[rt], b, st[rt].o[i]);
+            if constexpr (!pv_single(T, false)) st[rt].o[i] = mfma16x16x32<PT>(plo[rt], b, st[rt].o[i]);
+        }
     }
 }
 
@@ -892,7 +908,7 @@ template <int D>
 struct PSmem {
     uint4 k[kShareWaves][kBlk * D * 2 / 16];     // block j of the 64 tokens, loaded by wave j
     uint4 v[kShareWaves][kBlk * D * 2 / 16];
-    float corr[kShareWaves][16];                 // each wave's rescale slots
+    float corr[kShareWaves][32];                 // each wave's rescale slots, 16 per row tile
 };
 
 // Register budget: two waves per SIMD (two workgroups per CU).
@@ -968,13 +984,10 @@ shared_kv_mfma_kernel(const PartialParams pk) {
             if (tb >= wlen) break;                // the rest lie past this wave's rows
             const BlockRows ba = block_rows<D, PAGED>(p, pc, b, kvh, tb, t1);
             const BlockRows bb = block_rows<D, PAGED>(p, pc, b, kvh, tb + kBlk, t1);
-#pragma unroll
-            for (int rt = 0; rt < NT; ++rt)
-                compute_pair_at<T, D, GMAX>(p, ba, bb, lim[rt], sc, qop[rt], st[rt],
-                                            reinterpret_cast<const char *>(sm.k[j]),
-                                            reinterpret_cast<const char *>(sm.v[j]),
-                                            reinterpret_cast<const char *>(sm.k[j + 1]),
-                                            reinterpret_cast<const char *>(sm.v[j + 1]), sm.corr[w]);
+            compute_pair_at<T, D, GMAX>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[j]),
+                                        reinterpret_cast<const char *>(sm.v[j]),
+                                        reinterpret_cast<const char *>(sm.k[j + 1]),
+                                        reinterpret_cast<const char *>(sm.v[j + 1]), sm.corr[w]);
         }
         __syncthreads();                          // every wave's reads before the next writes
     }
