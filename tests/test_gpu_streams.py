@@ -27,22 +27,34 @@ def _gpu():
     fd.lib()
 
 
-def _inputs(page):
-    base = synth.Workload("streams", B=3, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=1, page_size=page)
+def _inputs(page, q_len=1, split=256):
+    base = synth.Workload("streams", B=3, Hq=32, Hkv=8, d=128, dtype="bf16", split=split, N=1, page_size=page,
+                          q_len=q_len)
     return synth.make_inputs(synth.with_lens(base, [4100, 517, 2049]))
 
 
-class _Call:
-    """One decode call (partial + combine, or the paged entry point) on fixed buffers."""
+# (page size, entry point) cases: partial + combine, the paged entry point
+# (AUTO), the contiguous fd_decode_attn with the single-launch merge (its
+# counters must come back to zero on every replay), and a one-split call
+# of 40 query tokens per request (query tiles sharing K and V, the result
+# written by the partial kernel)
+CASES = {"partial+combine": (0, "separate", 1, 256), "paged": (16, "auto", 1, 256),
+         "single launch": (0, "fused", 1, 256), "tiles, direct": (0, "auto", 40, 8192)}
 
-    def __init__(self, r: Run):
+
+class _Call:
+    """One decode call on fixed buffers: partial + combine, the paged entry
+    point, or the contiguous entry point with its merge mode."""
+
+    def __init__(self, r: Run, merge="separate"):
         import decode_attention_attn_amd as fd
         t = ft.torch()
         self.fd, self.r, w = fd, r, r.w
-        self.desc = r.desc()
-        self.out = t.empty((w.B, w.Hq, w.d), dtype=t.bfloat16, device="cuda")
-        self.lse = t.empty((w.B, w.Hq), dtype=t.float32, device="cuda")
-        if w.page_size:
+        self.merge = merge
+        self.desc = r.desc(merge=merge)
+        self.out = t.empty((w.B, w.q_len * w.Hq, w.d), dtype=t.bfloat16, device="cuda")
+        self.lse = t.empty((w.B, w.q_len * w.Hq), dtype=t.float32, device="cuda")
+        if w.page_size or merge != "separate":
             self.ws = fd.alloc_workspace(self.desc)
         else:
             self.po, self.pm, self.pl, _ = fd.alloc_partials(self.desc)
@@ -52,6 +64,8 @@ class _Call:
         if w.page_size:
             fd.fd_decode_attn_paged(self.desc, r.q, r.k, r.v, w.page_size, r.table, r.lens, self.ws, self.out,
                                     self.lse, stream=stream)
+        elif self.merge != "separate":
+            fd.fd_decode_attn(self.desc, r.q, r.k, r.v, w.N, r.lens, self.ws, self.out, self.lse, stream=stream)
         else:
             fd.fd_decode_attn_partial(self.desc, r.q, r.k, r.v, w.N, r.lens, self.po, self.pm, self.pl,
                                       stream=stream)
@@ -60,7 +74,7 @@ class _Call:
 
     def result(self):
         w = self.r.w
-        R = w.B * w.Hq
+        R = w.B * w.q_len * w.Hq
         return ft.f64(self.out).reshape(R, w.d), ft.f64(self.lse).reshape(R)
 
 
@@ -85,12 +99,13 @@ def test_side_stream_gives_the_default_stream_bits(page):
     ft.check_exact(dict(out=out, lse=lse), inp, what=f"side stream page={page}")
 
 
-@pytest.mark.parametrize("page", [0, 16])
-def test_captured_call_replays_like_eager(page):
+@pytest.mark.parametrize("case", list(CASES))
+def test_captured_call_replays_like_eager(case):
     t = ft.torch()
-    inp = _inputs(page)
+    page, merge, q_len, split = CASES[case]
+    inp = _inputs(page, q_len, split)
     r = Run(inp)
-    call = _Call(r)
+    call = _Call(r, merge)
     w = inp.w
     qs = [synth.normal(900 + i, inp.q.shape, w.q_dtype) for i in range(3)]
 
@@ -116,8 +131,8 @@ def test_captured_call_replays_like_eager(page):
         graph.replay()
         t.cuda.synchronize()
         out, lse = call.result()
-        say(f"[graph page={page}] replay {i}: max|out - eager| = {np.abs(out - ref_out).max():.3e}")
+        say(f"[graph {case}] replay {i}: max|out - eager| = {np.abs(out - ref_out).max():.3e}")
         assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse), f"replay {i}"
         if i == len(qs) - 1:
             ft.check_exact(dict(out=out, lse=lse), synth.Inputs(w, qi, inp.k, inp.v, inp.seq_lens,
-                                                                inp.block_table), what=f"graph page={page}")
+                                                                inp.block_table), what=f"graph {case}")
