@@ -5,9 +5,12 @@
 //
 // Work decomposition (as in the VALU kernel): one workgroup per (request b,
 // KV head, split s) covering all query rows of that KV head -- its G query
-// heads times the request's q_len query tokens, at most 32 -- so K and V are
-// read from HBM once per group (handbook page "FlashAttention and inference
-// kernels", exercise 3).  Each wave walks 16-token blocks of the split.
+// heads times the request's q_len query tokens, up to 32 rows; more rows go
+// in query tiles, each its own slice of the grid -- so K and V are read from
+// HBM once per group (handbook page "FlashAttention and inference kernels",
+// exercise 3).  Each wave walks 16-token blocks of the split.  Four or more
+// query tiles per KV head run in workgroups of four tiles that share each
+// K/V block (shared_kv_mfma_kernel below).
 // 8-bit (E4M3) caches are widened exactly to the 16-bit operand type in
 // registers before the LDS tiles; everything after the tiles is shared.
 //
@@ -29,10 +32,11 @@
 //   O[head][dim] += P V: D / 16 slices of v_mfma_f32_16x16x16.  The result
 //      layout of S^T is the A-operand layout of P (head l % 16, tokens
 //      4 * (l / 16) + e), so the probabilities stay in registers; they enter
-//      as a 16-bit high part plus the 16-bit rounding of the fp32 residual
-//      (two MFMAs), which keeps the weights to about 14 bits or better; with
-//      8-bit caches under the synchronized softmax, as one f16 operand
-//      rounded to nearest against f16 V tiles.
+//      for bf16 caches (and under unified max) as a 16-bit high part plus the
+//      16-bit rounding of the fp32 residual (two MFMAs), which keeps the
+//      weights to about 14 bits or better; with f16 and 8-bit caches under the
+//      synchronized softmax, as one f16 operand rounded to nearest against
+//      f16 V tiles.
 //      B (lane j of lane group q: V[token 4q + k][dim j] of the slice) comes
 //      from the V tile with ds_read_b64_tr_b16, whose result is lane j,
 //      element k = element j % 4 of the 8-byte row addressed by lane 4k + j / 4

@@ -865,6 +865,25 @@ def test_single_split_unified_max(kernel, fallback):
     ft.check_exact(res, inp, what=f"single split unified {kernel} {fallback}")
 
 
+@pytest.mark.parametrize("split,merge", [(65536, "auto"), (8192, "separate"), (8192, "fused")])
+def test_max_query_tokens(split, merge):
+    """The largest q_len (FD_MAX_Q_LEN = 65,536): a whole prompt of that
+    length as queries (2 query heads on 1 KV head, d=64), 2,048 query tiles
+    per KV head: one split (direct output from the groups sharing K/V),
+    eight splits with the combine, and eight with the single-launch merge.
+    Rows sampled across the prompt, the first and last tokens included,
+    against the oracle one by one."""
+    import decode_attention_attn_amd as fd
+    n = fd.MAX_Q_LEN
+    w = synth.Workload("qmax", B=1, Hq=2, Hkv=1, d=64, dtype="bf16", split=split, N=n, q_len=n)
+    inp = synth.make_inputs(w)
+    res = Run(inp).run(full=True, merge=merge)
+    assert res["desc"].max_splits == n // split
+    R = n * w.Hq
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(R - 8, R), ft.sample_rows(w, 240, seed=5)]))
+    ft.check_exact(res, inp, rows=rows.astype(np.int32), what=f"q_len={n} split={split} {merge}")
+
+
 def test_prefill_gqa_4k_full():
     """A whole 4k prompt as queries (32 heads on 8 KV heads, one split): every
     row against the oracle, through the AUTO entry point (direct output) and
