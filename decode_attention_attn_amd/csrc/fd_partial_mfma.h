@@ -508,13 +508,14 @@ __device__ __forceinline__ void compute_tiles_at(const PartialParams &p, const B
 // tokens of the first block (k = 8 (lane / 16) + 0..3) and its four of the
 // second (+ 4..7) in P and in V alike.  Half the P x V instructions of two
 // single-block steps, each doing twice the work; every K and V operand is
-// read from LDS once for all row tiles.  corr_lds: 16 slots per row tile.
+// read from LDS once for all row tiles.  The rescale factors reach the
+// accumulator lanes by lane shuffles (no LDS).
 template <int T, int D, int GMAX>
 __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const BlockRows &ba, const BlockRows &bb,
                                                 const int (&lim)[row_tiles(GMAX)], float sc,
                                                 const uint4 (&qop)[row_tiles(GMAX)][D / 32],
                                                 MState<D, GMAX> (&st)[row_tiles(GMAX)], const char *ka,
-                                                const char *va, const char *kb, const char *vb, float *corr_lds) {
+                                                const char *va, const char *kb, const char *vb) {
     using C = MCfg<D, GMAX, 1>;
     constexpr int DT = op_of(T), NT = row_tiles(GMAX);
     const int lane = threadIdx.x & 63;
@@ -567,10 +568,9 @@ __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const Bl
             }
         }
         if (__any(moved)) {
-            float *cs = corr_lds + 16 * rt;
-            if (lane < 16) cs[lane] = corr;
-            wave_lds_sync();
-            const float4 cf = *reinterpret_cast<const float4 *>(&cs[4 * mq]);
+            // rows 4 mq + 0..3 of this lane's accumulators; lane r (< 16) holds row r's factor
+            const float4 cf = make_float4(__shfl(corr, 4 * mq), __shfl(corr, 4 * mq + 1), __shfl(corr, 4 * mq + 2),
+                                          __shfl(corr, 4 * mq + 3));
 #pragma unroll
             for (int i = 0; i < C::SL; ++i) {
                 t.o[i][0] *= cf.x;
@@ -910,9 +910,11 @@ constexpr int kShareWaves = 4;
 
 template <int D>
 struct PSmem {
-    uint4 k[kShareWaves][kBlk * D * 2 / 16];     // block j of the 64 tokens, loaded by wave j
-    uint4 v[kShareWaves][kBlk * D * 2 / 16];
-    float corr[kShareWaves][32];                 // each wave's rescale slots, 16 per row tile
+    // two buffers of 64 tokens: the waves compute on one while the next is
+    // written to the other, one barrier per 64 tokens; block j of a buffer is
+    // loaded by wave j
+    uint4 k[2][kShareWaves][kBlk * D * 2 / 16];
+    uint4 v[2][kShareWaves][kBlk * D * 2 / 16];
 };
 
 // Register budget: two waves per SIMD (two workgroups per CU).
@@ -974,26 +976,30 @@ shared_kv_mfma_kernel(const PartialParams pk) {
     const int nsup = (t1 - t0 + W * kBlk - 1) / (W * kBlk);
     // one register set, as in the one-wave kernel: the next 64 tokens' loads
     // are in flight during the matrix work on these
-    BlockRows br = block_rows<D, PAGED>(p, pc, b, kvh, t0 + w * kBlk, t1);
+    const int tstep = W * kBlk;
     uint4 kr[L::LI], vr[L::LI];
-    load_block<T, D>(p, br, t1, off, kr, vr);
+    load_block<T, D>(p, block_rows<D, PAGED>(p, pc, b, kvh, t0 + w * kBlk, t1), t1, off, kr, vr);
+    write_tiles_at<T, D, false>(kr, vr, reinterpret_cast<char *>(sm.k[0][w]), reinterpret_cast<char *>(sm.v[0][w]));
+    __syncthreads();
+    load_block<T, D>(p, block_rows<D, PAGED>(p, pc, b, kvh, t0 + tstep + w * kBlk, t1), t1, off, kr, vr);
     for (int k = 0; k < nsup; ++k) {
-        const int tsup = t0 + k * W * kBlk;
-        write_tiles_at<T, D, false>(kr, vr, reinterpret_cast<char *>(sm.k[w]), reinterpret_cast<char *>(sm.v[w]));
-        __syncthreads();                          // all four blocks in LDS
-        const BlockRows bn = block_rows<D, PAGED>(p, pc, b, kvh, tsup + W * kBlk + w * kBlk, t1);
-        load_block<T, D>(p, bn, t1, off, kr, vr);
+        const int tsup = t0 + k * tstep, cur = k & 1;
         for (int j = 0; j < W; j += 2) {          // blocks in pairs: 32 tokens per matrix step
             const int tb = tsup + j * kBlk;
             if (tb >= wlen) break;                // the rest lie past this wave's rows
             const BlockRows ba = block_rows<D, PAGED>(p, pc, b, kvh, tb, t1);
             const BlockRows bb = block_rows<D, PAGED>(p, pc, b, kvh, tb + kBlk, t1);
-            compute_pair_at<T, D, GMAX>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[j]),
-                                        reinterpret_cast<const char *>(sm.v[j]),
-                                        reinterpret_cast<const char *>(sm.k[j + 1]),
-                                        reinterpret_cast<const char *>(sm.v[j + 1]), sm.corr[w]);
+            compute_pair_at<T, D, GMAX>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[cur][j]),
+                                        reinterpret_cast<const char *>(sm.v[cur][j]),
+                                        reinterpret_cast<const char *>(sm.k[cur][j + 1]),
+                                        reinterpret_cast<const char *>(sm.v[cur][j + 1]));
         }
-        __syncthreads();                          // every wave's reads before the next writes
+        // the next 64 tokens into the other buffer, whose last readers passed
+        // the previous barrier; then one barrier for both orders
+        write_tiles_at<T, D, false>(kr, vr, reinterpret_cast<char *>(sm.k[cur ^ 1][w]),
+                                    reinterpret_cast<char *>(sm.v[cur ^ 1][w]));
+        __syncthreads();
+        load_block<T, D>(p, block_rows<D, PAGED>(p, pc, b, kvh, tsup + 2 * tstep + w * kBlk, t1), t1, off, kr, vr);
     }
     if (R > 0) {
         const uint32_t all = R >= 32 ? 0xffffffffu : (1u << R) - 1u;
