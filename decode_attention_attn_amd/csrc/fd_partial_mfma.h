@@ -501,6 +501,8 @@ __device__ __forceinline__ void compute_tiles_at(const PartialParams &p, const B
     }
 }
 
+constexpr float kLazyRescale = 8.f;   // direct output: weights below 2^8, sums of up to 2^16 tokens in fp32
+
 // Two consecutive blocks (32 tokens) from their LDS tiles into the running
 // states of all of the wave's 16-row tiles, synchronized softmax: the scores
 // of both blocks, one running-max update for the 32, and O += P V on
@@ -509,8 +511,12 @@ __device__ __forceinline__ void compute_tiles_at(const PartialParams &p, const B
 // second (+ 4..7) in P and in V alike.  Half the P x V instructions of two
 // single-block steps, each doing twice the work; every K and V operand is
 // read from LDS once for all row tiles.  The rescale factors reach the
-// accumulator lanes by lane shuffles (no LDS).
-template <int T, int D, int GMAX>
+// accumulator lanes by lane shuffles (no LDS).  LAZY (a row's result written
+// directly, no partial): the reference maximum moves only when a score
+// exceeds it by more than kLazyRescale (log2 units), so weights stay below
+// 2^kLazyRescale and the rescale of the accumulators is rare; out = O / l and
+// lse = m + ln l do not depend on which reference m is used.
+template <int T, int D, int GMAX, bool LAZY = false>
 __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const BlockRows &ba, const BlockRows &bb,
                                                 const int (&lim)[row_tiles(GMAX)], float sc,
                                                 const uint4 (&qop)[row_tiles(GMAX)][D / 32],
@@ -553,7 +559,7 @@ __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const Bl
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         MState<D, GMAX> &t = st[rt];
-        const float mn = fmaxf(t.m, mt);
+        const float mn = (!LAZY || t.m == -INFINITY || mt > t.m + kLazyRescale) ? fmaxf(t.m, mt) : t.m;
         const float corr = rescale(t.m, mn);
         const bool moved = mn != t.m;
         t.m = mn;
@@ -989,7 +995,7 @@ shared_kv_mfma_kernel(const PartialParams pk) {
             if (tb >= wlen) break;                // the rest lie past this wave's rows
             const BlockRows ba = block_rows<D, PAGED>(p, pc, b, kvh, tb, t1);
             const BlockRows bb = block_rows<D, PAGED>(p, pc, b, kvh, tb + kBlk, t1);
-            compute_pair_at<T, D, GMAX>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[cur][j]),
+            compute_pair_at<T, D, GMAX, DIRECT>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[cur][j]),
                                         reinterpret_cast<const char *>(sm.v[cur][j]),
                                         reinterpret_cast<const char *>(sm.k[cur][j + 1]),
                                         reinterpret_cast<const char *>(sm.v[cur][j + 1]));

@@ -848,6 +848,20 @@ def test_direct_single_split(kernel, dtype, Hq, Hkv, q_len, d, page):
     ft.assert_close(res["lse"], sep["lse"], dtype, f"{what} lse vs separate")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_direct_tiles_with_score_spikes(dtype):
+    """One split per row, query tiles sharing K/V, direct output: the running
+    reference maximum moves only on jumps beyond 2^8 in the weights there.
+    Keys scaled x8 on 5% of the rows make the scores jump by tens of units
+    anywhere in the sequence; every row against the oracle."""
+    base = synth.Workload("spikes", B=1, Hq=32, Hkv=8, d=128, dtype=dtype, split=4096, N=1, q_len=64,
+                          stress_frac=0.05, stress_scale=8.0)
+    inp = synth.make_inputs(synth.with_lens(base, (3000, 64, 900)))
+    res = Run(inp).run(full=True)
+    assert res["desc"].max_splits == 1
+    ft.check_exact(res, inp, what=f"direct spikes {dtype}")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("fallback", ["split", "row"])
 def test_single_split_unified_max(kernel, fallback):
