@@ -990,9 +990,10 @@ shared_kv_mfma_kernel(const PartialParams pk) {
     load_block<T, D>(p, block_rows<D, PAGED>(p, pc, b, kvh, t0 + tstep + w * kBlk, t1), t1, off, kr, vr);
     for (int k = 0; k < nsup; ++k) {
         const int tsup = t0 + k * tstep, cur = k & 1;
+#pragma unroll
         for (int j = 0; j < W; j += 2) {          // blocks in pairs: 32 tokens per matrix step
             const int tb = tsup + j * kBlk;
-            if (tb >= wlen) break;                // the rest lie past this wave's rows
+            if (tb >= wlen) continue;             // past this wave's rows
             const BlockRows ba = block_rows<D, PAGED>(p, pc, b, kvh, tb, t1);
             const BlockRows bb = block_rows<D, PAGED>(p, pc, b, kvh, tb + kBlk, t1);
             compute_pair_at<T, D, GMAX, DIRECT>(p, ba, bb, lim, sc, qop, st, reinterpret_cast<const char *>(sm.k[cur][j]),
