@@ -972,6 +972,9 @@ def test_verify_tokens_long_context_gqa_full(name):
 HEURISTIC_CASES = [  # (B, Hq, Hkv, lens, page)
     ((1, 32, 8, (32768,), 0)), ((1, 8, 8, (700,), 0)), ((4, 32, 32, (4096, 100, 3000, 1), 0)),
     ((2, 64, 8, (9000, 2049), 16)), ((3, 16, 16, (77, 300, 129), 16)),
+    # a batch that fills the GPU several times over: one split per row (the paged
+    # entry point then writes the result from the partial kernel, no merge)
+    ((256, 32, 8, tuple(int(x) for x in np.random.default_rng(17).integers(1, 1001, 256)), 16)),
 ]
 
 
@@ -984,7 +987,8 @@ def test_heuristic_split_runs_and_matches_the_oracle(B, Hq, Hkv, lens, page):
     res = Run(inp).run()
     say(f"[heuristic] split={split} S={S} (cache S_max {res['part_m'].shape[1]})")
     ft.check_exact(res, inp, what=f"heuristic split {split}")
-    ft.check_partials(res, inp, split, what=f"heuristic split {split}")
+    if res["part_m"].shape[1] > 1 or not page:   # one split, paged (AUTO): no partials are written
+        ft.check_partials(res, inp, split, what=f"heuristic split {split}")
 
 
 # ----------------------------------------------------------------------------
