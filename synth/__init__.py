@@ -196,6 +196,11 @@ WORKLOADS = {
     "long_gqa_32k": Workload("long_gqa_32k", B=1, Hq=32, Hkv=8, d=128, dtype="bf16", split=256, N=32768),
     "paged_batched_gqa": Workload("paged_batched_gqa", B=64, Hq=64, Hkv=8, d=128, dtype="bf16", split=256,
                                   N=16384, len_range=(1024, 16384), page_size=16),
+    # a batch of short requests that fills the GPU many times over (256 x 8 KV heads): the split
+    # heuristic's one split per row (1008 tokens, page-aligned), where AUTO writes the result from
+    # the partial kernel with no merge (the Flash-Decoding page's no-split rule)
+    "paged_batch_short": Workload("paged_batch_short", B=256, Hq=32, Hkv=8, d=128, dtype="bf16", split=1008,
+                                  N=1008, len_range=(1, 1000), page_size=16),
     # no split size is given for this shape: 1024 is what the library's split heuristic picks for it
     "umax_stress": Workload("umax_stress", B=4, Hq=64, Hkv=8, d=128, dtype="bf16", split=1024, N=131072,
                             stress_frac=0.02, stress_scale=8.0),

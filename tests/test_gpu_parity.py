@@ -898,6 +898,22 @@ def test_max_query_tokens(split, merge):
     ft.check_exact(res, inp, rows=rows.astype(np.int32), what=f"q_len={n} split={split} {merge}")
 
 
+def test_paged_batch_short_full():
+    """256 short requests (1..1000 tokens, paged): one split per row, the
+    paged entry point's AUTO writes the result from the partial kernel;
+    every row against the oracle, and against the separate merge."""
+    w = synth.WORKLOADS["paged_batch_short"]
+    inp = synth.make_inputs(w)
+    run = Run(inp)
+    res = run.run()
+    assert res["desc"].max_splits == 1
+    e1, e2 = ft.check_exact(res, inp, what=w.name)
+    sep = run.run(merge="separate")
+    ft.check_exact(sep, inp, what=f"{w.name} separate")
+    ft.check_partials(sep, inp, w.split, what=w.name)
+    say(f"[{w.name}] max|out err|={e1:.3e} max|lse err|={e2:.3e}")
+
+
 def test_prefill_gqa_4k_full():
     """A whole 4k prompt as queries (32 heads on 8 KV heads, one split): every
     row against the oracle, through the AUTO entry point (direct output) and
