@@ -1026,6 +1026,18 @@ def test_fp8_per_head_scales(kernel, Hq, Hkv, d, qdt, page):
     ft.check_partials(res, inp, 128, what=what)
 
 
+@pytest.mark.parametrize("split,page", [(128, 0), (128, 16), (2048, 0), (2048, 16)])
+def test_fp8_per_head_scales_query_tiles(split, page):
+    """Per-head 8-bit scales with 40 query tokens per request: query tiles in
+    groups sharing K/V, writing partials (split 128) or the result directly
+    (split 2048, one split per row)."""
+    inp = _fp8_workload("fp8tiles", 3, 32, 8, 128, "bf16", (1000, 40, 385), page=page, split=split,
+                        k_scales=HEAD_KS, v_scales=HEAD_VS, q_len=40)
+    res = Run(inp).run(full=True)
+    what = f"fp8 per-head tiles split={split} page={page}"
+    ft.check_exact(res, inp, what=what)
+
+
 def test_fp8_per_head_scales_equal_to_the_tensor_scale_are_bitwise_the_same():
     """Per-head scales that all equal the tensor scale give the same bits as
     the tensor scale (power-of-two scales: the products are exact either way)."""
