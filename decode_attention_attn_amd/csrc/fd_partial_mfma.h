@@ -545,13 +545,25 @@ __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const Bl
         return make_uint4(u.x, u.y, w.x, w.y);
     };
     uint4 phi[NT], plo[NT];
+    const bool pages_ok = ba.page_ok && bb.page_ok;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
+        // Row 16 rt (lane 0) has the tile's smallest causal limit: when both
+        // blocks end below it every score of the pair is visible and no mask
+        // is applied (all but the blocks on the causal diagonal).
         float s[2][4];
+        if (pages_ok && bb.tb + kBlk <= __builtin_amdgcn_readfirstlane(lim[rt])) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[0][r] = ba.page_ok && ba.tb + 4 * mq + r < lim[rt] ? acc[rt][0][r] * sc : -INFINITY;
-            s[1][r] = bb.page_ok && bb.tb + 4 * mq + r < lim[rt] ? acc[rt][1][r] * sc : -INFINITY;
+            for (int r = 0; r < 4; ++r) {
+                s[0][r] = acc[rt][0][r] * sc;
+                s[1][r] = acc[rt][1][r] * sc;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[0][r] = ba.page_ok && ba.tb + 4 * mq + r < lim[rt] ? acc[rt][0][r] * sc : -INFINITY;
+                s[1][r] = bb.page_ok && bb.tb + 4 * mq + r < lim[rt] ? acc[rt][1][r] * sc : -INFINITY;
+            }
         }
         float mt = -INFINITY;
 #pragma unroll
@@ -564,12 +576,15 @@ __device__ __forceinline__ void compute_pair_at(const PartialParams &p, const Bl
         const bool moved = mn != t.m;
         t.m = mn;
         t.l *= corr;
+        // a row with no visible score yet (mn = -inf) has only -inf scores,
+        // whose weights exp2(-inf - 0) = 0 need a finite reference
+        const float mref = mn == -INFINITY ? 0.f : mn;
         float pr[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[h][r] = mn == -INFINITY ? 0.f : exp2_fast(s[h][r] - mn);
+                pr[h][r] = exp2_fast(s[h][r] - mref);
                 t.l += pr[h][r];
             }
         }
