@@ -743,10 +743,10 @@ QT_CASES = [  # (kernel, dtype, Hq, Hkv, q_len, d): tiles of the kernel's rows
 ]
 
 
-def _tile_inputs(dtype, Hq, Hkv, q_len, d, page=0, **kw):
+def _tile_inputs(dtype, Hq, Hkv, q_len, d, page=0, split=128, **kw):
     extra = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if dtype == "fp8" else {}
     extra.update(kw)
-    base = synth.Workload("qt", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=128, N=1, page_size=page,
+    base = synth.Workload("qt", B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, split=split, N=1, page_size=page,
                           q_len=q_len, **extra)
     # a request as long as its query tokens (a whole prompt), shorter ones (the
     # early tiles see nothing), and longer ones across split boundaries
@@ -765,6 +765,22 @@ def test_query_tiles(kernel, dtype, Hq, Hkv, q_len, d, page):
     r0 = (1 * q_len) * Hq
     n_blind = (q_len - 3) * Hq
     assert np.all(res["out"][r0:r0 + n_blind] == 0.0) and np.all(res["lse"][r0:r0 + n_blind] == -np.inf)
+
+
+@pytest.mark.parametrize("page", [32, 64])
+@pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", QT_CASES[8:11])
+def test_query_tile_groups_large_pages(kernel, dtype, Hq, Hkv, q_len, d, page):
+    """Tile groups sharing K/V blocks over pages of 32 and 64 tokens (each
+    16-token block inside one page, several blocks per page): split partials,
+    and with one split per row (split 1024) the result written directly."""
+    inp = _tile_inputs(dtype, Hq, Hkv, q_len, d, page)
+    what = f"tile groups q_len={q_len} {kernel} {dtype} d={d} page={page}"
+    res = Run(inp).run(kernel=kernel, merge="separate")
+    ft.check_exact(res, inp, what=what)
+    ft.check_partials(res, inp, 128, what=what)
+    inp = _tile_inputs(dtype, Hq, Hkv, q_len, d, page, split=1024)
+    res = Run(inp).run(kernel=kernel, full=True)
+    ft.check_exact(res, inp, what=what + " direct")
 
 
 @pytest.mark.parametrize("kernel,dtype,Hq,Hkv,q_len,d", [QT_CASES[0], QT_CASES[3], QT_CASES[4], QT_CASES[5]])
