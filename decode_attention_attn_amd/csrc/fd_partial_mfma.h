@@ -749,12 +749,15 @@ __device__ void finish_split(const PartialParams &p, MState<D, GMAX> &st, MSmem<
             for (int i = 0; i < C::SL; ++i) store_out(p.out, row * D + 16 * i + mrow, a[i] * inv, p.out_dtype);
             if (mrow == 0 && p.lse) p.lse[row] = L > 0.f ? m_nat + logf(L) : -INFINITY;
         } else {
+            // device-scope stores, written through the XCD's L2: a step (partials
+            // and their merge) measured ~1% faster than with plain stores, whose
+            // dirty lines the L2 writes back when the kernel ends
             const size_t slot = row_slot(p, b, kvh, g, s);
 #pragma unroll
-            for (int i = 0; i < C::SL; ++i) p.part_o[slot * D + 16 * i + mrow] = a[i] * inv;
+            for (int i = 0; i < C::SL; ++i) store_dev(&p.part_o[slot * D + 16 * i + mrow], a[i] * inv);
             if (mrow == 0) {
-                p.part_m[slot] = m_nat;
-                p.part_l[slot] = L;
+                store_dev(&p.part_m[slot], m_nat);
+                store_dev(&p.part_l[slot], L);
             }
         }
     }
