@@ -56,6 +56,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def default_merge(workload: str, split: int = 0, kernel: str = "auto") -> str:
+    """The merge mode a bench run uses unless told: contiguous caches time the
+    partial and combine kernels apart (the roofline is the partial kernel's),
+    except where the library's AUTO runs one kernel -- one split per row (the
+    partial kernel writes the result) and the VALU kernel (fp32 caches) with
+    at most 16 splits (its single launch) -- which, like a paged cache, run as
+    one call of the library."""
+    import synth
+    w0 = synth.WORKLOADS[workload]
+    n_splits = -(-w0.N // (split or w0.split))
+    valu = kernel == "valu" or (kernel == "auto" and w0.dtype == "f32")
+    one_kernel = n_splits == 1 or (valu and n_splits <= 16)
+    return "auto" if (w0.page_size or one_kernel) else "separate"
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -408,8 +423,9 @@ def main():
     ap.add_argument("--merge", default=None, choices=["separate", "fused", "auto"],
                     help="separate: a contiguous cache through the partial and combine entry points (two "
                          "launches, timed one by one); fused / auto: fd_decode_attn (or the paged entry point) "
-                         "with that merge mode.  Default: separate for a contiguous cache (what auto picks for "
-                         "the contiguous workloads), auto for a paged one")
+                         "with that merge mode.  Default: auto where it runs one kernel (a paged cache, one "
+                         "split per row, the VALU kernel with at most 16 splits), else separate (what auto "
+                         "picks there)")
     ap.add_argument("--split", type=int, default=0,
                     help="split size override (default: the workload's; a sweep knob, not the headline)")
     ap.add_argument("--warm", action="store_true", help="one KV copy (cache-resident for small caches)")
@@ -425,13 +441,7 @@ def main():
                     help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE runs into profiles/<workload>_pmc.json")
     args = ap.parse_args()
     if args.merge is None:
-        # contiguous caches: partial and combine timed apart (the roofline is the
-        # partial kernel's), except with one split per row, where the library
-        # writes the result from the partial kernel (AUTO) and has no combine
-        import synth
-        w0 = synth.WORKLOADS[args.workload]
-        one_split = -(-w0.N // (args.split or w0.split)) == 1
-        args.merge = "auto" if (w0.page_size or one_split) else "separate"
+        args.merge = default_merge(args.workload, args.split, args.kernel)
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)

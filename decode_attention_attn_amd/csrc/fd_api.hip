@@ -187,10 +187,14 @@ bool fused_fits(const fd::PartialParams &p, bool mfma) {
 // paged batch at split 256, 128 MiB of partial rows: 458 against 488 us per
 // call; B=4, N=128k at split 1024, 16 MiB: 368 against 361 us; 32k GQA,
 // 2 MiB: 29.6 against 29.1-29.3 us; Llama-2-shaped MHA, 256 KiB: 20.7
-// against 18.3-18.9 us.
+// against 18.3-18.9 us.  The VALU kernel's single launch keeps one split per
+// workgroup (no four-wave groups) and wins while the last workgroup merges
+// few splits: fp32 8-head MHA, N=512, 4 splits: 8.8-8.9 against 9.6 us;
+// Llama-2-shaped MHA on the VALU kernel, 16 splits: 19.5 against 19.8-19.9
+// us; 32k GQA on the VALU kernel, 128 splits: 46.6 against 40.8-41.1 us.
 bool fused_wanted(const fd_decode_desc *d, const fd::PartialParams &p, bool mfma) {
-    (void)mfma;
     if (d->merge != FD_MERGE_AUTO) return d->merge == FD_MERGE_FUSED;
+    if (!mfma && p.max_splits <= 16) return true;
     const double partial_bytes = (double)p.B * p.q_len * p.Hq * p.max_splits * p.d * sizeof(float);
     return partial_bytes >= 64.0 * (1 << 20);
 }

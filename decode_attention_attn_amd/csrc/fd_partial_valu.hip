@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     if (t0 >= t1) {   // empty split: nothing to read
         if (threadIdx.x < G && !p.recompute_rows) {
             const size_t slot = row_slot(p, b, kvh, threadIdx.x, s);
-            if (!FUSED && !p.direct) {
+            if (!p.direct) {   // the single launch's merge reads only splits with tokens
                 p.part_m[slot] = -INFINITY;
                 p.part_l[slot] = 0.f;
             }

@@ -110,3 +110,17 @@ def test_kernel_keys():
                             "(fd::CombineParams)") == "combine"
     assert bench.kernel_key("void fd::(anonymous namespace)::shared_kv_mfma_kernel<2, 128, false, true>"
                             "(fd::PartialParams)") == bench.PARTIAL_KERNEL
+
+
+def test_default_merge_follows_the_library_auto_choice():
+    """Two launches timed apart where AUTO merges separately; one call where
+    AUTO runs a single kernel (paged cache, one split per row, the VALU
+    kernel with at most 16 splits)."""
+    assert bench.default_merge("long_gqa_32k") == "separate"
+    assert bench.default_merge("llama2_7b_mha") == "separate"
+    assert bench.default_merge("llama2_7b_mha", kernel="valu") == "auto"       # 16 splits
+    assert bench.default_merge("long_gqa_32k", kernel="valu") == "separate"    # 128 splits
+    assert bench.default_merge("tiny_mha") == "auto"                           # fp32: VALU, 4 splits
+    assert bench.default_merge("prefill_gqa_4k") == "auto"                     # one split per row
+    assert bench.default_merge("paged_batched_gqa") == "auto"
+    assert bench.default_merge("long_gqa_32k", split=32768) == "auto"
