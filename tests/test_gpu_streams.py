@@ -27,19 +27,21 @@ def _gpu():
     fd.lib()
 
 
-def _inputs(page, q_len=1, split=256):
-    base = synth.Workload("streams", B=3, Hq=32, Hkv=8, d=128, dtype="bf16", split=split, N=1, page_size=page,
+def _inputs(page, q_len=1, split=256, dtype="bf16"):
+    base = synth.Workload("streams", B=3, Hq=32, Hkv=8, d=128, dtype=dtype, split=split, N=1, page_size=page,
                           q_len=q_len)
     return synth.make_inputs(synth.with_lens(base, [4100, 517, 2049]))
 
 
 # (page size, entry point) cases: partial + combine, the paged entry point
 # (AUTO), the contiguous fd_decode_attn with the single-launch merge (its
-# counters must come back to zero on every replay), and a one-split call
-# of 40 query tokens per request (query tiles sharing K and V, the result
-# written by the partial kernel)
-CASES = {"partial+combine": (0, "separate", 1, 256), "paged": (16, "auto", 1, 256),
-         "single launch": (0, "fused", 1, 256), "tiles, direct": (0, "auto", 40, 8192)}
+# counters must come back to zero on every replay), a one-split call of 40
+# query tokens per request (query tiles sharing K and V, the result written
+# by the partial kernel), and an fp32 cache under AUTO (the VALU kernel's
+# single launch, 5 splits)
+CASES = {"partial+combine": (0, "separate", 1, 256, "bf16"), "paged": (16, "auto", 1, 256, "bf16"),
+         "single launch": (0, "fused", 1, 256, "bf16"), "tiles, direct": (0, "auto", 40, 8192, "bf16"),
+         "fp32, VALU single launch": (0, "auto", 1, 1024, "f32")}
 
 
 class _Call:
@@ -52,7 +54,7 @@ class _Call:
         self.fd, self.r, w = fd, r, r.w
         self.merge = merge
         self.desc = r.desc(merge=merge)
-        self.out = t.empty((w.B, w.q_len * w.Hq, w.d), dtype=t.bfloat16, device="cuda")
+        self.out = t.empty((w.B, w.q_len * w.Hq, w.d), dtype=fd._tdtype(self.desc.out_dtype), device="cuda")
         self.lse = t.empty((w.B, w.q_len * w.Hq), dtype=t.float32, device="cuda")
         if w.page_size or merge != "separate":
             self.ws = fd.alloc_workspace(self.desc)
@@ -102,8 +104,8 @@ def test_side_stream_gives_the_default_stream_bits(page):
 @pytest.mark.parametrize("case", list(CASES))
 def test_captured_call_replays_like_eager(case):
     t = ft.torch()
-    page, merge, q_len, split = CASES[case]
-    inp = _inputs(page, q_len, split)
+    page, merge, q_len, split, dtype = CASES[case]
+    inp = _inputs(page, q_len, split, dtype)
     r = Run(inp)
     call = _Call(r, merge)
     w = inp.w
